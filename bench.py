@@ -1,0 +1,239 @@
+"""Throughput of the FlashAttention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one launch of the whole forward (scores, masks, online softmax,
+P V, normalisation, LSE) over one batch: B=4, H=16, N=4096, d=128 bf16,
+N(0,1) inputs, scale 1/sqrt(d), non-causal (the pages' N=4096, d=128 example
+shape, in bf16).  The causal variant of the same shape (1% of key rows x8)
+is timed too and reported in the "causal" object.  Inputs are resident in
+HBM before timing starts.
+
+Prints one JSON line with the headline metric (TFLOP/s, 4 B H N^2 d FLOPs,
+halved for causal), the matrix-core roofline of the kernel (dense bf16 peak
+of MI355X, 2.5 PFLOP/s), and the float64 CPU oracle timed on the host's cores
+over a bounded sample of the same workload.
+
+--profile-run launches a copy kernel of known size and then the forward a few
+times, without timing, for rocprofv3 counter collection (HBM bytes).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s at N=4096 d=128 bf16 (causal and non-causal), % MFMA peak"
+KERNEL_SOURCES = ("tiled_exact_attention_fwd_amd/csrc/fa_fwd_kernels.h",
+                  "tiled_exact_attention_fwd_amd/csrc/fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_n4096.json")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def upload(words, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(words.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(words).cuda()
+
+
+def time_workload(wl, causal, steps, warmup):
+    """Returns dict with ms_per_step (bracketed), per-launch mean/median ms."""
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    q, k, v = (upload(w, wl.dtype) for w in words)
+    o = torch.empty_like(q)
+    lse = torch.empty(wl.shape[:3], dtype=torch.float32, device=q.device)
+    scale = W.scale_for(wl.d)
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    code = fa.dtype_code(q.dtype)
+    B, H, N, d = wl.shape
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, H, N, d, scale, int(causal), handle, code)
+
+    def step():
+        st = fa.fa_fwd(*args)
+        if st != fa.FA_OK:
+            raise RuntimeError(f"fa_fwd failed: {fa.fa_strerror(st)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # bracketed region: exactly `steps` launches
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    bracket_ms = t0.elapsed_time(t1)
+    # per-launch durations, events on the launch stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        step()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    del q, k, v, o, lse
+    return dict(ms_per_step=bracket_ms / steps, launch_mean_ms=sum(per) / len(per),
+                launch_median_ms=per[len(per) // 2], launch_min_ms=per[0])
+
+
+def cpu_baseline(seconds):
+    """The float64 oracle on whole heads of the same workload, until about
+    `seconds` of CPU work; returns the oracle's TFLOP/s equivalent."""
+    import numpy as np
+    import fa_workloads as W
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    wl = W.WORKLOADS["C2b"]
+    B, H, N, d = wl.shape
+    rng = np.random.default_rng(W.default_seed())
+    scale = W.scale_for(d)
+    heads, t_total = 0, 0.0
+    while heads < B * H and (t_total < seconds or heads == 0):
+        q, k, v = (W.decode64(W.encode(rng.standard_normal((1, 1, N, d), dtype=np.float32), "bf16"), "bf16")
+                   for _ in range(3))
+        t = time.perf_counter()
+        oracle.attention_ref(q, k, v, scale, False)
+        t_total += time.perf_counter() - t
+        heads += 1
+    flops = 4.0 * N * N * d * heads
+    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{heads} head(s) of N={N}, d={d}, non-causal, float64 with S and P "
+                       f"materialised, {t_total:.1f} s",
+                seconds=t_total)
+
+
+def traffic_for_kernel():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def profile_run():
+    """Copy kernel of known size (counter calibration), then the forward."""
+    import torch
+    import fa_workloads as W
+    src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy kernel: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written", flush=True)
+    for name, causal in (("C2b", False), ("C3", True)):
+        r = time_workload(W.WORKLOADS[name], causal, 3, 1)
+        print(f"{name} causal={causal}: {r}", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(a.gpus, world)}): the forward "
+              "kernel runs on a single MI355X; multi-GPU sharding is not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    fa.lib()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if a.profile_run:
+        profile_run()
+        return
+
+    wl = W.WORKLOADS["C2b"]
+    r = time_workload(wl, False, a.steps, a.warmup)
+    flops = wl.flops(False)
+    value = flops / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (r["launch_mean_ms"] * 1e-3) / 1e12
+
+    wc = W.WORKLOADS["C3"]
+    rc = time_workload(wc, True, a.steps, a.warmup)
+    fc = wc.flops(True)
+    causal_value = fc / (rc["ms_per_step"] * 1e-3) / 1e12
+
+    traffic = traffic_for_kernel()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention forward B=4 H=16 N=4096 d=128 bf16 non-causal, "
+                               "Q/K/V i.i.d. N(0,1), scale 1/sqrt(128)",
+                   "B": 4, "H": 16, "N": 4096, "d": 128, "causal": False,
+                   "tile": list(fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 128, 0)[1:])},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic},
+        "causal": {"workload": "same shape, causal, 1% of key rows x8",
+                   "value": round(causal_value, 2), "unit": "TFLOP/s",
+                   "ms_per_step": round(rc["ms_per_step"], 5),
+                   "frac": round(fc / (rc["launch_mean_ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)},
+        "launch_ms": {"mean": round(r["launch_mean_ms"], 5), "median": round(r["launch_median_ms"], 5),
+                      "min": round(r["launch_min_ms"], 5)},
+        "hbm_min_gbs": round((4 * wl.B * wl.H * wl.N * wl.d * 2 + 4 * wl.B * wl.H * wl.N)
+                             / (r["launch_mean_ms"] * 1e-3) / 1e9, 1),
+        "kernel_hash": kernel_hash(),
+    }
+    if not a.no_cpu_baseline:
+        cb = cpu_baseline(a.cpu_seconds)
+        out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v)
+                               for k, v in cb.items() if k != "seconds"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -132,6 +132,12 @@ def scale_for(d):
     return float(np.float32(1.0 / np.sqrt(np.float64(d))))
 
 
+def make_words(shape, dtype, values="normal", seed=0):
+    """Encoded Q, K, V words for the device only (the oracle decodes the heads
+    it needs with ``decode64``)."""
+    return tuple(encode(t, dtype) for t in draw_f32(shape, values, seed))
+
+
 def make(shape, dtype, values="normal", seed=0):
     """Encoded Q, K, V words for the device and their exact float64 values
     for the oracle: returns ``(words, values64)``, each a (q, k, v) tuple."""

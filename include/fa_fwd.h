@@ -1,0 +1,158 @@
+/*
+ * fa_fwd.h -- C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * The operation (from "FlashAttention分块计算优化Transformer显存效率",
+ * §1.1 standard vs. tiled attention, §2.2 causal masking, §3.2 online
+ * softmax; and "Flash Attention 原理", blocked softmax and the statistics
+ * kept for a recomputing backward pass):
+ *
+ *   for every batch b and head h, with Q, K, V the N x d matrices of that head
+ *   (rows are tokens):
+ *     S      = scale * Q K^T                           (N x N, never stored)
+ *     S[i,j] = -inf where j > i                        (causal only; the
+ *                                                        diagonal is visible)
+ *     P      = row-softmax(S)                          (never stored)
+ *     O      = P V                                     (N x d, stored)
+ *     LSE[i] = ln sum_j exp(S[i,j])                    (stored, fp32)
+ *
+ * computed tile by tile with a running row maximum and running row sum that
+ * rescale a partial output; key tiles entirely above the diagonal are not
+ * loaded under the causal mask.
+ *
+ * Layout.  q, k, v and o are dense row-major [B, H, N, d] device arrays (each
+ * head is an N x d matrix with contiguous rows, element stride 1, row stride
+ * d).  lse is a dense [B, H, N] fp32 device array.  No other strides are
+ * accepted: a caller holding [B, N, H, d] makes it contiguous first.
+ *
+ * Element types.  fa_fwd_bf16 / fa_fwd_f16 / fa_fwd_f32 read bfloat16 /
+ * IEEE half / fp32 inputs and write o in the same type.  The products Q K^T
+ * and P V run on the matrix cores with fp32 accumulation; the softmax runs in
+ * fp32; P is rounded (to nearest even) to the input type before P V, and o
+ * is rounded to nearest even on store.  fp32 inputs use fp32 matrix-core
+ * arithmetic throughout.
+ *
+ * Sizes.  B, H, N, d > 0.  d must be 64 or 128.  N * d * elem_size must be
+ * below 2^31 bytes per head, and B * H * ceil(N / tile_q) below 2^31.
+ *
+ * Ownership and concurrency.  The caller allocates every buffer.  The library
+ * allocates no device memory, keeps no per-call state and may be called from
+ * several host threads.  Work is enqueued on `stream` (a hipStream_t passed
+ * as an opaque pointer; NULL is the default stream) and the call returns
+ * without synchronising.  q, k and v may alias one another; o and lse must
+ * not overlap any input or each other.
+ *
+ * Errors.  Every argument check runs before any HIP call and returns
+ * synchronously; nothing is enqueued when a check fails.  The library never
+ * prints and never throws.  A fault inside a kernel surfaces at the caller's
+ * next synchronisation.  Non-finite input values propagate to the outputs of
+ * the rows that see them; they are not masked.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID = 1,      /* B, H, N or d <= 0 (sizes must be positive),
+                                a NULL pointer, causal not 0 or 1, scale not
+                                finite, o / lse overlapping an input or each
+                                other, unknown out_dtype                     */
+    FA_ERR_UNSUPPORTED = 2,  /* d not 64 or 128, unknown dtype, tile shape not
+                                built, sizes beyond the limits above, device
+                                not gfx950                                    */
+    FA_ERR_HIP = 3           /* a HIP runtime call (device query or kernel
+                                launch) failed                               */
+} fa_status;
+
+/* Element types of q, k, v (and of o unless out_dtype says fp32). */
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2 } fa_dtype;
+
+/* Indices into the optional tile-counter array of fa_fwd_ex. */
+enum {
+    FA_COUNT_COMPUTED = 0,      /* (query tile, key tile) pairs processed     */
+    FA_COUNT_FULL = 1,          /* ... of which unmasked and full length      */
+    FA_COUNT_CAUSAL_MASKED = 2, /* ... of which reach past the diagonal       */
+    FA_COUNT_RAGGED = 3,        /* ... of which are the short last key tile   */
+    FA_COUNT_SKIPPED = 4,       /* pairs above the diagonal, never loaded     */
+    FA_NUM_COUNTERS = 5
+};
+
+/*
+ * The forward pass, one entry point per element type, with the parameter list
+ * of the problem statement:
+ *   q, k, v  device pointers to [B, H, N, d] inputs (read only)
+ *   o        device pointer to the [B, H, N, d] output, same element type
+ *   lse      device pointer to the [B, H, N] fp32 log-sum-exp output
+ *   B, H, N, d  batch, heads, sequence length, head dimension
+ *   scale    multiplies Q K^T (1/sqrt(d) in the pages); any finite value
+ *   causal   0: every key visible; 1: key j visible to query i iff j <= i
+ *   stream   hipStream_t (opaque), or NULL
+ * Returns an fa_status.
+ */
+int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal, void* stream);
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* The same twelve parameters followed by the element type (an fa_dtype). */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream,
+           int dtype);
+
+/*
+ * Extended form for validation and measurement.  Same semantics, plus:
+ *   out_dtype  0: o has the input element type; 1: o is fp32 (the output is
+ *              then not rounded to 16 bits -- used to check the kernel's
+ *              arithmetic separately from the final rounding)
+ *   tile_q, tile_k  0 selects the library default; otherwise the shape must
+ *              be one that was built (see fa_fwd_tile_shape)
+ *   counters   NULL for the plain kernel; otherwise a device array of
+ *              FA_NUM_COUNTERS unsigned 64-bit integers to which the launch
+ *              ADDS its tile counts (indices above).  The caller zeroes it.
+ *              A separately compiled instrumented kernel is used; the plain
+ *              kernel carries no counting code.
+ */
+typedef struct {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N, d;
+    float scale;
+    int causal;
+    void* stream;
+    int dtype;
+    int out_dtype;
+    int tile_q, tile_k;
+    unsigned long long* counters;
+} fa_fwd_args;
+
+int fa_fwd_ex(const fa_fwd_args* args);
+
+/*
+ * The (tile_q, tile_k) shape a launch with these parameters uses by default,
+ * so the caller can compute the expected tile counts.  Pure host function,
+ * no HIP call.  Returns FA_OK, or FA_ERR_UNSUPPORTED / FA_ERR_INVALID with
+ * the outputs untouched.
+ */
+int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k);
+
+/* Static description of a status code; never NULL. */
+const char* fa_strerror(int status);
+
+/* Static description of the build: offload architecture, compile flags and
+ * the kernel instances built.  Never NULL. */
+const char* fa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

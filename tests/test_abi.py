@@ -1,0 +1,123 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/fa_fwd.h declares, and rejects bad arguments before any HIP call
+(sizes must be positive, as the memory-model page's helpers require; null
+pointers; bad flags; overlapping outputs; unsupported shapes)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_exact_attention_fwd_amd as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fa_fwd.h")
+
+# fake, well separated device addresses: validation never dereferences them
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fa.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in fa.SIGNATURES, f"binding lacks {n}"
+    # and the binding offers a function of the same name for each
+    for n in names:
+        assert callable(getattr(fa, n))
+
+
+def test_build_info_and_strerror():
+    assert "gfx950" in fa.fa_build_info()
+    for st in (fa.FA_OK, fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, 99):
+        assert isinstance(fa.fa_strerror(st), str) and fa.fa_strerror(st)
+
+
+def test_tile_shape():
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_F32, 64, 0) == (fa.FA_OK, 64, 64)
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 128, 1) == (fa.FA_OK, 128, 64)
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_F16, 64, 0) == (fa.FA_OK, 128, 128)
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 96, 0)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_tile_shape(7, 64, 0)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 64, 2)[0] == fa.FA_ERR_INVALID
+
+
+def call(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+             stream=None, dtype=fa.FA_DTYPE_BF16)
+    a.update(over)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                     a["d"], a["scale"], a["causal"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("field", ["B", "H", "N", "d"])
+@pytest.mark.parametrize("value", [0, -1])
+def test_nonpositive_sizes_are_invalid(field, value):
+    assert call(**{field: value}) == fa.FA_ERR_INVALID
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_pointers_are_invalid(field):
+    assert call(**{field: None}) == fa.FA_ERR_INVALID
+
+
+def test_flags_and_scale():
+    assert call(causal=2) == fa.FA_ERR_INVALID
+    assert call(causal=-1) == fa.FA_ERR_INVALID
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert call(scale=bad) == fa.FA_ERR_INVALID
+
+
+def test_unsupported_shapes_and_types():
+    assert call(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    # per-head extent beyond 2^31 bytes
+    assert call(N=1 << 22, d=128) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_overlapping_outputs_are_invalid():
+    nbytes = 2 * 3 * 100 * 64 * 2
+    assert call(o=Q) == fa.FA_ERR_INVALID
+    assert call(o=Q + nbytes - 2) == fa.FA_ERR_INVALID           # tail overlap
+    assert call(lse=V + 16) == fa.FA_ERR_INVALID
+    assert call(lse=O + 8) == fa.FA_ERR_INVALID                  # o and lse overlap
+    # q, k, v may alias one another (read only): rejected only later, for lack of a GPU
+    st = call(k=Q, v=Q)
+    assert st in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)
+
+
+def test_ex_argument_checks():
+    def ex(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=256, d=64, scale=0.125, causal=0,
+                 stream=None, dtype=fa.FA_DTYPE_F32)
+        a.update(over)
+        return fa.fa_fwd_ex(**a)
+    assert ex(out_dtype=2) == fa.FA_ERR_INVALID
+    assert ex(tile_q=32, tile_k=64) == fa.FA_ERR_UNSUPPORTED
+    assert ex(tile_q=-1) == fa.FA_ERR_INVALID
+    assert fa.lib().fa_fwd_ex(None) == fa.FA_ERR_INVALID
+
+
+def test_per_dtype_entry_points_share_validation():
+    for fn in (fa.fa_fwd_bf16, fa.fa_fwd_f16, fa.fa_fwd_f32):
+        assert fn(Q, K, V, O, L, 0, 1, 1, 64, 1.0, 0, None) == fa.FA_ERR_INVALID
+        assert fn(Q, K, V, O, L, 1, 1, 1, 48, 1.0, 0, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(fa.FaLibraryMissing):
+        fa.lib(str(tmp_path / "nope.so"))
+
+
+def test_struct_layout_matches_header():
+    # 5 pointers, 4 ints, float, int, pointer, 4 ints, pointer on LP64
+    assert ctypes.sizeof(fa.FaArgs) == 5 * 8 + 4 * 4 + 4 + 4 + 8 + 4 * 4 + 8

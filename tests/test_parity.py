@@ -1,0 +1,230 @@
+"""GPU parity of the HIP forward pass against the float64 oracle.
+
+Every launch goes through the C ABI (ctypes binding).  Inputs are the seeded
+words of fa_workloads, uploaded as-is and decoded exactly for the oracle.
+Gates are described in parity_util: G1 (fp32-output launch within the
+tolerance), G2 (16-bit output within tolerance beyond its own half ulp), LSE
+within 1e-3; tile counts bit-exact against oracle.block_counts at the shape
+the library reports.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import oracle
+import tiled_exact_attention_fwd_amd as fa
+from parity_util import (TOL_O, TOL_LSE, assert_gates, gate_errors, out_to64,
+                         sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+CODE = {"f32": fa.FA_DTYPE_F32, "f16": fa.FA_DTYPE_F16, "bf16": fa.FA_DTYPE_BF16}
+
+
+def expected_counts(dtype, d, N, causal, heads):
+    st, tq, tk = fa.fa_fwd_tile_shape(CODE[dtype], d, int(causal))
+    assert st == fa.FA_OK
+    c = oracle.block_counts(N, tq, tk, causal)
+    return {k: v * heads for k, v in c.items()}
+
+
+def launch_all(qd, kd, vd, dtype, causal, scale):
+    """Plain launch (output in the input type), fp32-output launch, and the
+    instrumented launch; returns (o, lse, o32, lse32, counts)."""
+    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale)
+    if dtype == "f32":
+        o32, lse32 = o, lse
+    else:
+        o32, lse32 = fa.attention(qd, kd, vd, causal=causal, scale=scale, out_f32=True)
+    oc, lsec, cnt = fa.attention(qd, kd, vd, causal=causal, scale=scale, counters=True)
+    torch.cuda.synchronize()
+    # the instrumented kernel computes exactly what the plain one does
+    assert torch.equal(oc.view(torch.int16) if dtype != "f32" else oc, o.view(torch.int16) if dtype != "f32" else o)
+    assert torch.equal(lsec, lse)
+    return o, lse, o32, lse32, cnt
+
+
+def check_against_oracle(words, dtype, causal, scale, rows=None, heads=None, what=""):
+    B, H, N, d = words[0].shape
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    o, lse, o32, lse32, cnt = launch_all(qd, kd, vd, dtype, causal, scale)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
+    o32_np = out_to64(o32)
+    worst = {}
+    for b, h in heads:
+        vals = [W.decode64(w[b, h], dtype)[None, None] for w in words]
+        o_ref, lse_ref = oracle.attention_ref(*vals, scale, causal, rows=rows)
+        sel = slice(None) if rows is None else rows
+        errs = gate_errors(o32_np[b, h, sel][None, None], None if dtype == "f32" else o_np[b, h, sel][None, None],
+                           lse_np[b, h, sel][None, None], o_ref, lse_ref, dtype)
+        assert_gates(errs, dtype, f"{what} head ({b},{h})")
+        for k_, v_ in errs.items():
+            worst[k_] = max(worst.get(k_, 0.0), v_)
+    assert cnt == expected_counts(dtype, d, N, causal, B * H), f"{what} counts {cnt}"
+    return worst, (qd, kd, vd, o, lse, o32)
+
+
+# ---------------------------------------------------------------------------
+# Small shapes: several tiles, ragged tails, every instance; full oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 128, 200, 257])
+def test_small_16bit(dtype, d, causal, N):
+    words = W.make_words((2, 2, N, d), dtype, "normal", seed=N + d)
+    worst, _ = check_against_oracle(words, dtype, causal, W.scale_for(d), what=f"N={N} d={d}")
+    print(f"{dtype} d={d} causal={causal} N={N}: {worst}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 256, 300])
+def test_small_f32(d, causal, N):
+    words = W.make_words((1, 3, N, d), "f32", "normal", seed=N + d)
+    worst, _ = check_against_oracle(words, "f32", causal, W.scale_for(d), what=f"N={N} d={d}")
+    # fp32 matrix-core arithmetic: far inside the stated gate
+    assert worst["g1"] < 1e-4 and worst["lse"] < 1e-4, worst
+    print(f"f32 d={d} causal={causal} N={N}: {worst}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_spiky_and_scales(dtype):
+    """Running-max rescales (a few keys x8), a negative scale, a large scale
+    that makes the softmax nearly one-hot."""
+    words = W.make_words((1, 2, 300, 128), dtype, "spiky", seed=5)
+    check_against_oracle(words, dtype, True, W.scale_for(128), what="spiky")
+    words = W.make_words((1, 2, 190, 64), dtype, "normal", seed=6)
+    check_against_oracle(words, dtype, False, -0.2, what="negative scale")
+    check_against_oracle(words, dtype, True, 2.0, what="large scale")
+
+
+# ---------------------------------------------------------------------------
+# The named workloads at full size, launched as the benchmark launches them;
+# sampled rows against the oracle, properties on every row
+# ---------------------------------------------------------------------------
+
+WORKLOAD_CASES = [("C1", False), ("C1", True), ("C2", False), ("C2b", False), ("C3", True),
+                  ("C4", False), ("C4", True), ("C5", True)]
+
+
+@pytest.mark.parametrize("name,causal", WORKLOAD_CASES)
+def test_workload(name, causal):
+    wl = W.WORKLOADS[name]
+    print(f"workload {name} causal={causal} shape={wl.shape} dtype={wl.dtype}", flush=True)
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    rng = np.random.default_rng(123)
+    B, H, N, d = wl.shape
+    allh = [(b, h) for b in range(B) for h in range(H)]
+    if len(allh) <= 4:
+        heads, rows = allh, (None if N <= 1024 else sample_rows(N, 64, rng))
+    else:
+        pick = rng.choice(len(allh), 3, replace=False)
+        heads = sorted({allh[0], allh[-1]} | {allh[i] for i in pick})
+        rows = sample_rows(N, 64, rng)
+    worst, (qd, kd, vd, o, lse, o32) = check_against_oracle(
+        words, wl.dtype, causal, W.scale_for(d), rows=rows, heads=heads, what=name)
+    print(f"{name} causal={causal}: {worst}")
+    # every row: the output is a convex combination of the visible value rows
+    vf = vd.float()
+    if causal:
+        lo, hi = torch.cummin(vf, dim=2).values, torch.cummax(vf, dim=2).values
+    else:
+        lo, hi = vf.amin(dim=2, keepdim=True), vf.amax(dim=2, keepdim=True)
+    tol = TOL_O[wl.dtype]
+    assert bool((o32 >= lo - tol).all()) and bool((o32 <= hi + tol).all())
+    assert bool(torch.isfinite(lse).all())
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and degenerate cases, no oracle needed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_closed_forms(dtype, d):
+    B, H, N = 2, 2, 333
+    words = W.make_words((B, H, N, d), dtype, "normal", seed=11)
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    v64 = W.decode64(words[2], dtype)
+    q64, k64 = W.decode64(words[0], dtype), W.decode64(words[1], dtype)
+    tol = TOL_O[dtype]
+    # scale 0: uniform weights over the visible keys
+    for causal in (False, True):
+        o32, lse = fa.attention(qd, kd, vd, causal=causal, scale=0.0, out_f32=(dtype != "f32"))
+        cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+        ref = (np.cumsum(v64, axis=2) if causal else np.sum(v64, axis=2, keepdims=True)) / cnt[:, None]
+        assert np.max(np.abs(out_to64(o32) - ref)) <= tol
+        assert np.max(np.abs(lse.cpu().numpy() - np.log(cnt))) <= TOL_LSE
+    # causal row 0 sees only key 0: O_0 = V_0 exactly, LSE_0 = scale q0.k0
+    s = W.scale_for(d)
+    o, lse = fa.attention(qd, kd, vd, causal=True, scale=s)
+    if dtype == "f32":
+        # P_00 = 2^(s c - round(s c)) is 1 only to within an fp32 rounding
+        assert torch.allclose(o[:, :, 0], vd[:, :, 0], rtol=4e-7, atol=0)
+    else:
+        # P_00 rounds to exactly 1 in 16 bits, so O_0 is V_0 bit for bit
+        assert torch.equal(o[:, :, 0].float(), vd[:, :, 0].float())
+    ref = s * np.einsum("bhd,bhd->bh", q64[:, :, 0], k64[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0].cpu().numpy() - ref)) <= TOL_LSE
+    # identical key rows: uniform attention whatever the queries
+    kk = kd[:, :, :1].expand(-1, -1, N, -1).contiguous()
+    o32, lse = fa.attention(qd, kk, vd, causal=False, scale=s, out_f32=(dtype != "f32"))
+    assert np.max(np.abs(out_to64(o32) - v64.mean(axis=2, keepdims=True))) <= tol
+    dots = s * np.einsum("bhnd,bhd->bhn", q64, k64[:, :, 0])
+    assert np.max(np.abs(lse.cpu().numpy() - (dots + math.log(N)))) <= TOL_LSE
+
+
+def test_deterministic_and_entry_points_agree():
+    """Repeated launches are bitwise identical (no LDS race shows up as
+    run-to-run noise); the per-type entry points, the generic one and the
+    extended one give the same bits."""
+    words = W.make_words((4, 8, 1000, 64), "bf16", "normal", seed=3)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    s = W.scale_for(64)
+    o1, l1 = fa.attention(qd, kd, vd, causal=True, scale=s)
+    for _ in range(2):
+        o2, l2 = fa.attention(qd, kd, vd, causal=True, scale=s)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    stream = torch.cuda.current_stream().cuda_stream
+    for dtype, fn in (("bf16", fa.fa_fwd_bf16), ("f16", fa.fa_fwd_f16), ("f32", fa.fa_fwd_f32)):
+        w = W.make_words((1, 2, 130, 128), dtype, "normal", seed=4)
+        qd, kd, vd = (to_dev(x, dtype) for x in w)
+        ref_o, ref_l = fa.attention(qd, kd, vd, causal=False, scale=0.1)
+        o = torch.empty_like(ref_o)
+        lse = torch.empty_like(ref_l)
+        args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                1, 2, 130, 128, 0.1, 0, stream)
+        assert fn(*args) == fa.FA_OK
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+        o.zero_()
+        assert fa.fa_fwd(*args, CODE[dtype]) == fa.FA_OK
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o)
+
+
+def test_guard_bands_untouched():
+    """Ragged N: nothing is written outside o and lse."""
+    B, H, N, d = 3, 5, 1000, 64
+    words = W.make_words((B, H, N, d), "bf16", "normal", seed=9)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    pad = 4096
+    n_o, n_l = B * H * N * d, B * H * N
+    obuf = torch.full((n_o + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((n_l + 2 * pad,), -3.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n_o].view(B, H, N, d)
+    lse = lbuf[pad:pad + n_l].view(B, H, N)
+    for causal in (False, True):
+        fa.attention(qd, kd, vd, causal=causal, o=o, lse=lse)
+        torch.cuda.synchronize()
+        assert bool((obuf[:pad] == 7.0).all()) and bool((obuf[pad + n_o:] == 7.0).all())
+        assert bool((lbuf[:pad] == -3.0).all()) and bool((lbuf[pad + n_l:] == -3.0).all())
+        assert bool(torch.isfinite(o.float()).all())

@@ -1,0 +1,177 @@
+"""Python binding of ``libfa_fwd.so``, the MI355X (gfx950) FlashAttention
+forward library whose C ABI is ``include/fa_fwd.h``.
+
+The functions named like the C entry points (``fa_fwd_bf16``, ``fa_fwd_f16``,
+``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_tile_shape``,
+``fa_strerror``, ``fa_build_info``) only marshal arguments: pointers are
+plain integers (device addresses), the stream an integer ``hipStream_t``
+handle, and the C status code is returned unchanged.
+
+``attention(q, k, v, ...)`` is a convenience on top for torch tensors: it
+allocates the outputs with torch (device memory only), passes torch's current
+stream, and raises on a non-zero status.  Every step of the computation runs
+in the HIP kernels; there is no fallback.  If the library has not been built
+the import of this package still succeeds but every call raises
+``FaLibraryMissing`` (build with ``python -m tiled_exact_attention_fwd_amd.build``).
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+COUNTER_NAMES = ("computed", "full", "causal_masked", "ragged", "skipped")
+
+# entry point name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_FWD12 = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]
+
+
+class FaArgs(ctypes.Structure):
+    """Mirror of ``fa_fwd_args``."""
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P),
+                ("B", _I), ("H", _I), ("N", _I), ("d", _I),
+                ("scale", _F), ("causal", _I), ("stream", _P),
+                ("dtype", _I), ("out_dtype", _I), ("tile_q", _I), ("tile_k", _I),
+                ("counters", _P)]
+
+
+SIGNATURES = {
+    "fa_fwd_bf16": (_I, _FWD12),
+    "fa_fwd_f16": (_I, _FWD12),
+    "fa_fwd_f32": (_I, _FWD12),
+    "fa_fwd": (_I, _FWD12 + [_I]),
+    "fa_fwd_ex": (_I, [ctypes.POINTER(FaArgs)]),
+    "fa_fwd_tile_shape": (_I, [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "fa_strerror": (ctypes.c_char_p, [_I]),
+    "fa_build_info": (ctypes.c_char_p, []),
+}
+
+
+class FaLibraryMissing(ImportError):
+    pass
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({fa_strerror(status)})")
+
+
+_lib = None
+
+
+def lib(path=None):
+    """Load (once) and return the ctypes handle of libfa_fwd.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FaLibraryMissing(
+            f"{p} not found: build it with `python -m tiled_exact_attention_fwd_amd.build`")
+    handle = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype, fn.argtypes = res, args
+    if path is None:
+        _lib = handle
+    return handle
+
+
+# --- thin wrappers with the C names -----------------------------------------
+
+def fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    return lib().fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    return lib().fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
+    return lib().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype):
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype)
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
+              out_dtype=0, tile_q=0, tile_k=0, counters=None):
+    a = FaArgs(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
+               out_dtype, tile_q, tile_k, counters)
+    return lib().fa_fwd_ex(ctypes.byref(a))
+
+
+def fa_fwd_tile_shape(dtype, d, causal):
+    """Returns ``(status, tile_q, tile_k)``."""
+    tq, tk = _I(0), _I(0)
+    st = lib().fa_fwd_tile_shape(dtype, d, causal, ctypes.byref(tq), ctypes.byref(tk))
+    return st, tq.value, tk.value
+
+
+def fa_strerror(status):
+    return lib().fa_strerror(status).decode()
+
+
+def fa_build_info():
+    return lib().fa_build_info().decode()
+
+
+# --- torch convenience (device memory and streams only) ---------------------
+
+def dtype_code(torch_dtype):
+    import torch
+    codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if torch_dtype not in codes:
+        raise ValueError(f"unsupported element type {torch_dtype}")
+    return codes[torch_dtype]
+
+
+def attention(q, k, v, causal=False, scale=None, out_f32=False, counters=False,
+              o=None, lse=None, stream=None):
+    """Exact attention forward on the device.
+
+    q, k, v: contiguous [B, H, N, d] CUDA(HIP) tensors of one dtype (fp32, fp16
+    or bf16).  Returns ``(o, lse)``, or ``(o, lse, counts)`` with ``counts`` a
+    dict of tile counts when ``counters`` is set (that launch uses the
+    instrumented kernel).  ``o`` / ``lse`` may be passed in preallocated.
+    """
+    import math
+    import torch
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = dtype_code(q.dtype)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    cnt = torch.zeros(len(COUNTER_NAMES), dtype=torch.int64, device=q.device) if counters else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   B, H, N, d, float(scale), int(bool(causal)), stream, dt,
+                   out_dtype=1 if out_f32 else 0,
+                   counters=cnt.data_ptr() if cnt is not None else None)
+    if st == FA_ERR_INVALID:
+        raise ValueError(f"fa_fwd: {fa_strerror(st)}")
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    if counters:
+        vals = cnt.cpu().tolist()
+        return o, lse, dict(zip(COUNTER_NAMES, vals))
+    return o, lse

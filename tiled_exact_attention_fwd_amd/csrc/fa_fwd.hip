@@ -1,0 +1,217 @@
+// Host layer of the C ABI declared in include/fa_fwd.h: argument checks (all
+// before any HIP call), kernel-instance selection, launch on the caller's
+// stream.  No allocation, no synchronisation, no printing.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa_fwd.h"
+#include "fa_fwd_kernels.h"
+
+#ifndef FA_BUILD_FLAGS
+#define FA_BUILD_FLAGS "unknown"
+#endif
+
+namespace {
+
+using fa::BF16;
+using fa::F16;
+using fa::FwdParams;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+int elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Default (and only built) tile shape per element type and head dimension.
+void tile_shape(int dtype, int d, int* tq, int* tk) {
+    if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
+    else { *tq = 128; *tk = 8192 / d; }
+}
+
+int check_args(const fa_fwd_args* a) {
+    if (!a) return FA_ERR_INVALID;
+    if (a->B <= 0 || a->H <= 0 || a->N <= 0 || a->d <= 0) return FA_ERR_INVALID;
+    if (!a->q || !a->k || !a->v || !a->o || !a->lse) return FA_ERR_INVALID;
+    if (a->causal != 0 && a->causal != 1) return FA_ERR_INVALID;
+    if (!std::isfinite(a->scale)) return FA_ERR_INVALID;
+    if (a->out_dtype != 0 && a->out_dtype != 1) return FA_ERR_INVALID;
+    if (a->dtype != FA_DTYPE_F32 && a->dtype != FA_DTYPE_F16 && a->dtype != FA_DTYPE_BF16)
+        return FA_ERR_UNSUPPORTED;
+    if (a->d != 64 && a->d != 128) return FA_ERR_UNSUPPORTED;
+    int tq, tk;
+    tile_shape(a->dtype, a->d, &tq, &tk);
+    if (a->tile_q < 0 || a->tile_k < 0) return FA_ERR_INVALID;
+    if ((a->tile_q && a->tile_q != tq) || (a->tile_k && a->tile_k != tk)) return FA_ERR_UNSUPPORTED;
+    const int e = elem_size(a->dtype);
+    if ((uint64_t)a->N * a->d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;   // per-head bytes
+    const uint64_t tiles = (uint64_t)a->B * a->H * (uint64_t)((a->N + tq - 1) / tq);
+    if (tiles >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    const uint64_t elems = (uint64_t)a->B * a->H * a->N * a->d;
+    const uint64_t in_b = elems * e;
+    const uint64_t out_b = elems * (a->out_dtype ? 4 : e);
+    const uint64_t lse_b = (uint64_t)a->B * a->H * a->N * 4;
+    const void* ins[3] = {a->q, a->k, a->v};
+    for (const void* in : ins) {
+        if (overlaps(a->o, out_b, in, in_b)) return FA_ERR_INVALID;
+        if (overlaps(a->lse, lse_b, in, in_b)) return FA_ERR_INVALID;
+    }
+    if (overlaps(a->o, out_b, a->lse, lse_b)) return FA_ERR_INVALID;
+    return FA_OK;
+}
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+template <class K>
+int launch(const FwdParams& p, void* stream) {
+    void* args[] = {const_cast<FwdParams*>(&p)};
+    const hipError_t err = hipLaunchKernel((const void*)&fa::fwd_kernel<K>, dim3(p.total), dim3(K::NT),
+                                          args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <class T, int D, bool CAUSAL>
+int pick16(const FwdParams& p, int out_f32, bool count, void* stream) {
+    if (out_f32) {
+        return count ? launch<fa::Fwd16<T, D, CAUSAL, true, true>>(p, stream)
+                     : launch<fa::Fwd16<T, D, CAUSAL, true, false>>(p, stream);
+    }
+    return count ? launch<fa::Fwd16<T, D, CAUSAL, false, true>>(p, stream)
+                 : launch<fa::Fwd16<T, D, CAUSAL, false, false>>(p, stream);
+}
+
+template <class T, int D>
+int pick16c(const FwdParams& p, int causal, int out_f32, bool count, void* stream) {
+    return causal ? pick16<T, D, true>(p, out_f32, count, stream)
+                  : pick16<T, D, false>(p, out_f32, count, stream);
+}
+
+template <int D, bool CAUSAL>
+int pick32(const FwdParams& p, bool count, void* stream) {
+    return count ? launch<fa::Fwd32<D, CAUSAL, true>>(p, stream)
+                 : launch<fa::Fwd32<D, CAUSAL, false>>(p, stream);
+}
+
+int run(const fa_fwd_args* a) {
+    int st = check_args(a);
+    if (st != FA_OK) return st;
+    st = check_device();
+    if (st != FA_OK) return st;
+
+    int tq, tk;
+    tile_shape(a->dtype, a->d, &tq, &tk);
+    FwdParams p;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.o = a->o;
+    p.lse = a->lse;
+    p.N = a->N;
+    p.tiles_q = (a->N + tq - 1) / tq;
+    p.total = a->B * a->H * p.tiles_q;
+    // softmax in base 2: exp(scale * s) = 2^(s * |scale| * log2 e) after a sign
+    // flip of Q for negative scales; FLT_MIN keeps -inf * c at -inf for scale 0
+    p.c = std::fmax(std::fabs(a->scale) * 1.4426950408889634f, FLT_MIN);
+    const bool neg = a->scale < 0.f;
+    p.qsign = neg ? (a->dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u) : 0u;
+    p.counters = a->counters;
+    const bool count = a->counters != nullptr;
+
+    switch (a->dtype) {
+    case FA_DTYPE_BF16:
+        return a->d == 64 ? pick16c<BF16, 64>(p, a->causal, a->out_dtype, count, a->stream)
+                          : pick16c<BF16, 128>(p, a->causal, a->out_dtype, count, a->stream);
+    case FA_DTYPE_F16:
+        return a->d == 64 ? pick16c<F16, 64>(p, a->causal, a->out_dtype, count, a->stream)
+                          : pick16c<F16, 128>(p, a->causal, a->out_dtype, count, a->stream);
+    default:
+        if (a->d == 64)
+            return a->causal ? pick32<64, true>(p, count, a->stream) : pick32<64, false>(p, count, a->stream);
+        return a->causal ? pick32<128, true>(p, count, a->stream) : pick32<128, false>(p, count, a->stream);
+    }
+}
+
+fa_fwd_args plain_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                       int N, int d, float scale, int causal, void* stream, int dtype) {
+    fa_fwd_args a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.scale = scale; a.causal = causal; a.stream = stream; a.dtype = dtype;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_ex(const fa_fwd_args* args) { return run(args); }
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, void* stream, int dtype) {
+    const fa_fwd_args a = plain_args(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
+    return run(&a);
+}
+
+int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, void* stream) {
+    return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, FA_DTYPE_BF16);
+}
+
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+    return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, FA_DTYPE_F16);
+}
+
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+    return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, FA_DTYPE_F32);
+}
+
+int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k) {
+    if (!tile_q || !tile_k || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    tile_shape(dtype, d, tile_q, tile_k);
+    return FA_OK;
+}
+
+const char* fa_strerror(int status) {
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* fa_build_info(void) {
+    return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
+           "; kernels: bf16/f16 d64 (128x128 tiles) and d128 (128x64 tiles), causal on/off, "
+           "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off";
+}
+
+}  // extern "C"
