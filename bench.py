@@ -34,7 +34,9 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s at N=4096 d=128 bf16 (causal and non-causal), % MFMA peak"
 KERNEL_SOURCES = ("tiled_exact_attention_fwd_amd/csrc/fa_fwd_kernels.h",
                   "tiled_exact_attention_fwd_amd/csrc/fa_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_d128_n4096.json")
+# the instance bench.py times for the headline (bf16, d=128, non-causal)
+HEADLINE_KERNEL = "fa::BF16, 128, false, false, false"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_n4096_counters.txt")
 
 
 def kernel_hash():
@@ -130,17 +132,84 @@ def cpu_baseline(seconds):
                 seconds=t_total)
 
 
-def traffic_for_kernel():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel sources changed since the counters were taken."""
+def read_summary(path):
+    """`key: value` lines of a profile summary (other lines ignored)."""
+    out = {}
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+        with open(path) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith((" ", "#", "|")):
+                    k, v = ln.split(":", 1)
+                    out[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return out
+
+
+def traffic_for_kernel():
+    """HBM bytes per launch of the C2b kernel from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since the
+    counters were taken."""
+    t = read_summary(TRAFFIC_FILE)
+    if t.get("kernel_hash") != kernel_hash() or "hbm_bytes_per_launch" not in t:
         return None
-    if t.get("kernel_hash") != kernel_hash():
-        return None
-    return t.get("bytes_per_launch")
+    return int(t["hbm_bytes_per_launch"])
+
+
+def summarize(kind, paths):
+    """Text summary of rocprofv3 output for profiles/.
+    kind 'trace': a --kernel-trace --stats directory (csv output).
+    kind 'counters': the FETCH_SIZE and WRITE_SIZE --pmc directories (csv),
+    scaled by what the same counters read for the copy kernel of known size
+    that --profile-run launches first."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit(f"no {pattern} under {d}")
+        with open(files[0]) as f:
+            return list(csv.DictReader(f))
+
+    if kind == "trace":
+        for r in rows(paths[0], "*kernel_stats.csv"):
+            name = r["Name"]
+            if "fa::" not in name:
+                continue
+            print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        return
+    per = {}
+    for d in paths:
+        for r in rows(d, "*counter_collection.csv"):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
+    copy_bytes = 64 * (1 << 20) * 4
+    fetch_copy = statistics.median(v for (k, c), vals in per.items() if "copyBuffer" in k and c == "FETCH_SIZE"
+                                   for v in vals)
+    write_copy = statistics.median(v for (k, c), vals in per.items() if "copyBuffer" in k and c == "WRITE_SIZE"
+                                   for v in vals)
+    f_fetch = copy_bytes / (fetch_copy * 1024)
+    f_write = copy_bytes / (write_copy * 1024)
+    print(f"kernel_hash: {kernel_hash()}")
+    print(f"copy_fetch_factor: {f_fetch:.4f}")
+    print(f"copy_write_factor: {f_write:.4f}")
+    total = 0.0
+    for (k, c), vals in per.items():
+        if HEADLINE_KERNEL in k:
+            total += statistics.median(vals) * 1024 * (f_fetch if c == "FETCH_SIZE" else f_write)
+    print(f"hbm_bytes_per_launch: {int(round(total))}")
+    print()
+    print("| kernel | counter | dispatches | median raw | scaled |")
+    print("|---|---|---|---|---|")
+    for (k, c), vals in sorted(per.items()):
+        if "fa::" not in k:
+            continue
+        scale = f_fetch if c == "FETCH_SIZE" else f_write
+        print(f"| {k} | {c} | {len(vals)} | {statistics.median(vals):.0f} KiB | "
+              f"{statistics.median(vals) * 1024 * scale / (1 << 20):.2f} MiB scaled |")
 
 
 def profile_run():
@@ -167,7 +236,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="print a profiles/ summary of rocprofv3 csv output: "
+                         "'trace DIR' or 'counters FETCH_DIR WRITE_DIR'")
     a = ap.parse_args()
+    if a.summarize:
+        summarize(a.summarize[0], a.summarize[1:])
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(a.gpus, world)}): the forward "
