@@ -36,7 +36,7 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 // Default (and only built) tile shape per element type and head dimension.
 void tile_shape(int dtype, int d, int* tq, int* tk) {
     if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
-    else { *tq = 128; *tk = 8192 / d; }
+    else { *tq = 128; *tk = 64; }
 }
 
 int check_args(const fa_fwd_args* a) {
@@ -210,7 +210,7 @@ const char* fa_strerror(int status) {
 
 const char* fa_build_info(void) {
     return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
-           "; kernels: bf16/f16 d64 (128x128 tiles) and d128 (128x64 tiles), causal on/off, "
+           "; kernels: bf16/f16 d64 and d128 (128x64 tiles), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off";
 }
 

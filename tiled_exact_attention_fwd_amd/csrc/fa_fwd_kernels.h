@@ -79,7 +79,9 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 // combinations below are the same bits in both half-waves.
 __device__ __forceinline__ float max_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float m;
+    asm volatile("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 __device__ __forceinline__ float sum_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -149,42 +151,219 @@ struct FwdParams {
 
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16)
+//
+// One workgroup = 4 waves = a 128-row query tile of one (batch, head); each
+// wave owns 32 query rows for the whole key loop.  Key tiles are 64 rows.
+//
+// Per key tile t a wave does three things: the scores S_t = K_t Q^T (16 MFMA
+// at d = 128), the online softmax of S_t (VALU), and O += V_t^T P_t^T (16
+// MFMA).  They are software-pipelined one tile apart, so that iteration j
+// issues the score MFMAs of tile j+1 and the output MFMAs of tile j-1 while
+// the VALU works on the softmax of tile j: the three streams are independent
+// within an iteration, and the MFMAs are interleaved one by one with the
+// softmax instructions (a wave co-issues its own VALU work under a running
+// MFMA).
+//
+// K and V tiles are copied HBM -> LDS by the buffer unit directly (no VGPR
+// staging), double-buffered: iteration j reads K_{j+1} and V_{j-1} and fills
+// the other halves with K_{j+2} and V_j; one barrier per iteration.  K rows
+// are stored with their 16-byte chunks XOR-swizzled by row so that the
+// 16-byte operand reads of 16 lanes hit distinct banks; V is stored row-major
+// (swizzled the same way for its own access pattern) and read transposed with
+// ds_read_b64_tr_b16, which hands every lane four consecutive keys of one
+// head-dimension column -- the V^T operand of the second product.
+//
+// The reference maximum of a row is raised only when a tile's maximum exceeds
+// it by more than 2^8 in the exponent (in units of the base-2 exponent).  Until
+// then the unnormalised terms exp2(c s - c m_ref) stay below 2^8, and the
+// running output and sum need no rescale: the result is the same up to
+// rounding, since numerator and denominator share the reference.
 // ---------------------------------------------------------------------------
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2_t lds_read_tr(const uint8_t* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(__attribute__((address_space(3))) uint8_t*)p);
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+// max(a, b, c) in one instruction (no NaN canonicalisation of the inputs)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// keeps a value's computation at this point of the instruction stream: the
+// compiler may not sink it past here (the MFMA interleave depends on it)
+template <class X> __device__ __forceinline__ void pin(X& x) { asm volatile("" : "+v"(x)); }
+
+constexpr float kRescaleThreshold = 8.0f;
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };   // log2 of the largest unnormalised term
 
 template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT>
 struct Fwd16 {
     static constexpr int BQ = 128;                 // query rows per workgroup
     static constexpr int WAVES = 4;
-    static constexpr int OCC = 2;                  // waves per SIMD (<= 256 VGPRs)
+    static constexpr int OCC = 2;                  // waves per SIMD (<= 256 registers each)
     static constexpr int NT = 64 * WAVES;
-    static constexpr int BK = 8192 / D;            // keys per tile: tile_k x d = 16 KiB
-    static constexpr int KCH = D / 8;              // 16-byte chunks per K row
-    static constexpr int VCH = BK / 8;             // 16-byte chunks per V^T row
+    static constexpr int BK = 64;                  // keys per tile
+    static constexpr int ROWB = 2 * D;             // bytes per K / V row
+    static constexpr int TILEB = BK * ROWB;        // bytes per K or V tile
+    static constexpr int NS = D / 16;              // k-steps of K Q^T per 32-key block
+    static constexpr int NDB = D / 32;             // 32-row d blocks of O^T
     static constexpr int NMB = BK / 32;            // 32-key blocks per tile
-    static constexpr int NS = D / 16;              // k-steps of Q K^T
-    static constexpr int NDB = D / 32;             // 32-wide d blocks of O^T
-    static constexpr int KBYTES = BK * D * 2;
-    static constexpr int BUFBYTES = 2 * KBYTES;    // K + V^T
-    static constexpr int LDS = 2 * BUFBYTES;       // double buffered
-    static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert((BK / 8) * (D / 8) == 128, "V staging assumes 128 threads");
+    static constexpr int NKS = BK / 16;            // k-steps of V^T P^T per tile
+    static constexpr int NPV = NDB * NKS;          // output MFMAs per tile
+    static constexpr int NQK = NMB * NS;           // score MFMAs per tile
+    static constexpr int NSLOT = NPV + NQK;
+    static constexpr int NV = BK / 2;              // scores per lane per tile
+    static constexpr int LOADS = TILEB / (NT * 16);// 16-byte copies per thread per tile
+    static constexpr int PD = 3;                   // operand prefetch distance (MFMA slots)
+    static constexpr int LDS = 4 * TILEB;
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile copy");
 
-    // row permutation of the K operand: swap bits 2 and 3
+    // K row permutation: swap bits 2 and 3, so that each half-wave's eight
+    // consecutive score registers hold eight consecutive keys
     static __device__ __forceinline__ int perm_row(int r) {
         return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
     }
-    // XOR swizzles of the 16-byte chunk index (conflict-free 16-lane reads)
-    static __device__ __forceinline__ int swz_k(int r) {
-        return D == 128 ? (perm_row(r) & 15) : ((r >> 1) & 7);
+    // chunk swizzles (16-byte chunk index XOR f(row))
+    static __device__ __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+    struct Lane {
+        int koff[NS];       // K operand byte offsets within a tile, per k-step
+        int voff[NDB];      // V^T operand byte offsets within a tile, per d block
+    };
+
+    // Per-lane source offset (within a tile) of this lane's 16-byte copies:
+    // the copies of a thread are 4 KiB apart in LDS, i.e. a multiple of 16
+    // rows apart, which leaves the swizzle of the row unchanged; so one offset
+    // serves all of them.
+    template <bool ISK>
+    static __device__ __forceinline__ uint32_t copy_offset(int wave, int lane) {
+        const int off = wave * 1024 + lane * 16;
+        const int row = off / ROWB, pos = (off % ROWB) >> 4;
+        const int chunk = pos ^ (ISK ? fk(row) : fv(row));
+        return (uint32_t)(row * ROWB + chunk * 16);
     }
-    static __device__ __forceinline__ int swz_v(int d) {
-        return D == 128 ? (((d >> 1) ^ (d >> 4)) & 7) : ((d ^ (d >> 3)) & 15);
+    // One tile HBM -> LDS; every thread issues LOADS 16-byte copies.  The
+    // whole offset goes in the VGPR operand: the buffer unit range-checks
+    // that one against the head's extent (reads past row N return zero), so
+    // no part of it may be moved to the scalar offset.
+    static __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, int k0,
+                                                     int wave, uint32_t src) {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int blk = u * WAVES + wave;             // 1 KiB block of the tile
+            uint32_t off = src + (uint32_t)(k0 * ROWB + u * WAVES * 1024);
+            asm volatile("" : "+v"(off));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(lbuf + blk * 1024), 16, off, 0, 0, 0);
+        }
+    }
+
+    static __device__ __forceinline__ u32x4_t k_operand(const uint8_t* kb, const Lane& ln, int mb, int ks) {
+        return *(const u32x4_t*)(kb + ln.koff[ks] + 32 * mb * ROWB);
+    }
+    static __device__ __forceinline__ u32x4_t v_operand(const uint8_t* vb, const Lane& ln, int db, int kt) {
+        const uint8_t* p = vb + ln.voff[db] + 16 * kt * ROWB;
+        const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 4 * ROWB);
+        return u32x4_t{a[0], a[1], b[0], b[1]};
+    }
+
+    // the MFMA of one slot: slots [0, NPV) are O^T += V^T P^T (k-step major, so
+    // consecutive MFMAs go to different accumulators), the rest S^T = K Q^T
+    static __device__ __forceinline__ void slot_mfma(int i, u32x4_t a, f32x16_t* acc, f32x16_t* snext,
+                                                     const u32x4_t* pprev, const u32x4_t* qreg) {
+        if (i < NPV) {
+            const int kt = i / NDB, db = i % NDB;
+            acc[db] = mma<T>(a, pprev[kt], acc[db]);
+        } else {
+            const int q = i - NPV, ks = q / NMB, mb = q % NMB;
+            snext[mb] = mma<T>(a, qreg[ks], ks == 0 ? f32x16_t{} : snext[mb]);
+        }
+    }
+    static __device__ __forceinline__ u32x4_t slot_operand(int i, const uint8_t* kb, const uint8_t* vb,
+                                                           const Lane& ln) {
+        if (i < NPV) return v_operand(vb, ln, i % NDB, i / NDB);
+        const int q = i - NPV;
+        return k_operand(kb, ln, q % NMB, q / NMB);
+    }
+
+    // softmax state of one lane (one query row; both half-waves hold it)
+    struct Soft {
+        float mc;      // reference maximum times c (base-2 exponent units)
+        float l;       // running sum of this half-wave's terms
+        float alpha;   // rescale factor of the current tile
+        float mxa, mxb;
+        float meff;    // mc, or +inf when this iteration has no tile (terms are 0)
+        bool need;
+        bool live;     // this iteration has a tile of this wave
+    };
+
+    // VALU work of the softmax, split into groups spread over the MFMA slots:
+    // groups [0, NV/2) fold two scores into the row maximum, group NV/2 makes
+    // the new reference and the correction, groups after it turn two scores
+    // into two terms, round them to 16 bits, pack them and add them to l.
+    static constexpr int NG = NV / 2 + 1 + NV / 2;
+    static constexpr int cost(int g) { return g < NV / 2 ? 1 : (g == NV / 2 ? 8 : 7); }
+    static constexpr int cum(int g) { return g == 0 ? 0 : cum(g - 1) + cost(g - 1); }
+    static constexpr int group_slot(int g) { return cum(g) * NSLOT / cum(NG); }
+    // the term registers of k-step kt are rewritten only after the last
+    // output MFMA that reads them (slot kt * NDB + NDB - 1)
+    static constexpr bool terms_after_reads() {
+        for (int k = 0; k < NV / 2; ++k)
+            if (group_slot(NV / 2 + 1 + k) <= (k / 4) * NDB + NDB - 1) return false;
+        return true;
+    }
+    static_assert(terms_after_reads(), "softmax would overwrite terms before the output MFMA reads them");
+
+    static __device__ __forceinline__ void valu_group(int g, const f32x16_t* scur, u32x4_t* pcur,
+                                                      Soft& st, float c) {
+        auto val = [&](int v) { return scur[v / 16][v % 16]; };
+        if (g < NV / 2) {
+            float& m = (g & 1) ? st.mxb : st.mxa;
+            m = max3(m, val(2 * g), val(2 * g + 1));
+        } else if (g == NV / 2) {
+            float mx;
+            asm volatile("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(st.mxa), "v"(st.mxb));
+            mx = max_halves(mx);
+            const float mxc = mx * c;
+            st.need = st.live && mxc > st.mc + kRescaleThreshold;
+            const float nmc = st.need ? mxc : st.mc;
+            st.alpha = st.need ? __builtin_amdgcn_exp2f(st.mc - nmc) : 1.0f;
+            st.mc = nmc;
+            st.meff = st.live ? nmc : __builtin_inff();
+            st.l *= st.alpha;
+            pin(st.meff);
+            pin(st.l);
+        } else {
+            const int k = g - NV / 2 - 1;   // pair index: scores 2k, 2k+1
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(val(2 * k), c, -st.meff));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(val(2 * k + 1), c, -st.meff));
+            // the sum takes the fp32 terms: the log-sum-exp has to hold to
+            // 1e-3, which the 16-bit rounding of a dominant term would not
+            uint32_t pk = pack2<T>(p0, p1);
+            st.l += p0;
+            st.l += p1;
+            pin(pk);
+            pin(st.l);
+            pcur[k / 4][k % 4] = pk;
+        }
     }
 
     static __device__ void run(const FwdParams& p) {
-        __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+        __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TILEB];
         const int tid = threadIdx.x;
-        const int wave = tid >> 6, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
         const int li = lane & 31, lh = lane >> 5;
         const int N = p.N;
 
@@ -197,10 +376,28 @@ struct Fwd16 {
         const int qrow = q0w + li;
 
         const size_t head_elems = (size_t)hh * N * D;
-        const uint32_t head_bytes = (uint32_t)N * D * 2;
+        const uint32_t head_bytes = (uint32_t)N * ROWB;
         const auto rq = make_rsrc((const uint8_t*)p.q + head_elems * 2, head_bytes);
         const auto rk = make_rsrc((const uint8_t*)p.k + head_elems * 2, head_bytes);
         const auto rv = make_rsrc((const uint8_t*)p.v + head_elems * 2, head_bytes);
+
+        const int nk = (N + BK - 1) / BK;
+        const int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        // key tiles this wave computes (all of them, up to its diagonal when causal)
+        int wend = q0w < N ? (CAUSAL ? min(jend, (q0w + 31) / BK + 1) : jend) : 0;
+        wend = __builtin_amdgcn_readfirstlane(wend);
+
+        // Both V buffers start as zeros: the first two iterations multiply
+        // them with zero terms, and rows past N of a ragged last tile stay
+        // zero whether or not the copy unit writes out-of-range rows.  The K
+        // buffer that may be read before it is first filled starts as zeros
+        // too, so that every score is finite.
+#pragma unroll
+        for (int i = tid; i < TILEB / 16; i += NT) {
+            ((u32x4_t*)vbuf0)[i] = u32x4_t{0, 0, 0, 0};
+            ((u32x4_t*)vbuf1)[i] = u32x4_t{0, 0, 0, 0};
+            ((u32x4_t*)kbuf1)[i] = u32x4_t{0, 0, 0, 0};
+        }
 
         // Q^T operand: lane (li, lh) holds Q[qrow][16 s + 8 lh .. +7]
         u32x4_t qreg[NS];
@@ -210,147 +407,124 @@ struct Fwd16 {
             qreg[s] ^= p.qsign;
         }
 
-        const int nk = (N + BK - 1) / BK;
-        const int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
-
-        // staging roles: threads 0..127 stage K, 128..255 stage V
-        const bool stage_k = tid < 128;
-        const int st = tid & 127;
-        u32x4_t stg[8];
-
-        auto gload = [&](int j) {
-            const int k0 = j * BK;
-            if (stage_k) {
+        Lane ln;
+        {
+            const int prow = perm_row(li);
+            const int ks_sw = fk(prow);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int id = st + 128 * u, row = id / KCH, c = id % KCH;
-                    stg[u] = buf_load16(rk, (uint32_t)((k0 + row) * D + c * 8) * 2);
-                }
-            } else {
-                const int kg = st / (D / 8), dc = st % (D / 8);
+            for (int ks = 0; ks < NS; ++ks) ln.koff[ks] = prow * ROWB + (((2 * ks + lh) ^ ks_sw) << 4);
+            const int G = lane >> 4, s = lane & 15;
+            const int fvq = D == 128 ? ((s >> 2) & 3) : ((s >> 3) & 1);
+            const int y = 2 * (G & 1) + ((s & 3) >> 1);
 #pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    stg[r] = buf_load16(rv, (uint32_t)((k0 + 8 * kg + r) * D + 8 * dc) * 2);
-            }
-        };
-        auto lstore = [&](int buf) {
-            uint8_t* kb = smem + buf * BUFBYTES;
-            uint8_t* vb = kb + KBYTES;
-            if (stage_k) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int id = st + 128 * u, row = id / KCH, c = id % KCH;
-                    *(u32x4_t*)(kb + row * (D * 2) + ((c ^ swz_k(row)) << 4)) = stg[u];
-                }
-            } else {
-                // 8 keys x 8 d  ->  8 d-rows x 8 keys (V^T)
-                const int kg = st / (D / 8), dc = st % (D / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4_t w;
-#pragma unroll
-                    for (int kp = 0; kp < 4; ++kp)
-                        w[kp] = __builtin_amdgcn_perm(stg[2 * kp + 1][e >> 1], stg[2 * kp][e >> 1], sel);
-                    const int d = 8 * dc + e;
-                    *(u32x4_t*)(vb + d * (BK * 2) + ((kg ^ swz_v(d)) << 4)) = w;
-                }
-            }
-        };
+            for (int db = 0; db < NDB; ++db)
+                ln.voff[db] = (8 * lh + (s >> 2)) * ROWB + ((4 * (db ^ fvq) + y) << 4) + 8 * (s & 1);
+        }
 
         f32x16_t acc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
-        float m = -__builtin_inff(), l = 0.f;
+        f32x16_t s0[NMB], s1[NMB];     // scores of even / odd tiles
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) s0[mb] = s1[mb] = f32x16_t{};
+        // packed terms: the output MFMAs of an iteration read the previous
+        // tile's terms from the same registers the softmax then overwrites
+        // with this tile's (each k-step's registers only after their last read)
+        u32x4_t pk[NKS];
+#pragma unroll
+        for (int kt = 0; kt < NKS; ++kt) pk[kt] = u32x4_t{0, 0, 0, 0};
+        Soft st;
+        st.mc = -__builtin_inff();
+        st.l = 0.f;
+        st.alpha = 1.f;
         const float c = p.c;
 
-        gload(0);
-        lstore(0);
-        __syncthreads();
+        const uint32_t ksrc = copy_offset<true>(wave, lane);
+        const uint32_t vsrc = copy_offset<false>(wave, lane);
 
-        for (int j = 0; j < jend; ++j) {
-            const int buf = j & 1;
-            if (j + 1 < jend) gload(j + 1);
-            const uint8_t* kb = smem + buf * BUFBYTES;
-            const uint8_t* vb = kb + KBYTES;
+        // prologue: K_0 into kbuf0
+        copy_tile(rk, kbuf0, 0, wave, ksrc);
+
+        // iteration j (see the header comment); ODD selects the buffers / arrays
+        auto iteration = [&](const int j, auto odd_tag) {
+            constexpr bool ODD = decltype(odd_tag)::value;
+            uint8_t* kread = ODD ? kbuf0 : kbuf1;      // K_{j+1}
+            uint8_t* kfill = ODD ? kbuf1 : kbuf0;      // K_{j+2}
+            uint8_t* vread = ODD ? vbuf0 : vbuf1;      // V_{j-1}
+            uint8_t* vfill = ODD ? vbuf1 : vbuf0;      // V_j
+            f32x16_t* scur = ODD ? s1 : s0;
+            f32x16_t* snext = ODD ? s0 : s1;
+            u32x4_t* pprev = pk;
+            u32x4_t* pcur = pk;
+
+            __syncthreads();   // this wave's copies done (vmcnt 0), and everyone's
+            if (j + 2 < jend) copy_tile(rk, kfill, (j + 2) * BK, wave, ksrc);
+            if (j >= 0 && j < jend) copy_tile(rv, vfill, j * BK, wave, vsrc);
+
+            // Every iteration runs the same straight-line schedule (one
+            // register allocation, no divergent code paths).  Where a stream
+            // has nothing to do its work is made harmless instead of skipped:
+            // the softmax of an iteration without a tile of this wave sees
+            // need = false and a reference of +inf, so its terms are exactly 0
+            // and its state is unchanged; the output MFMAs then add 0 * V
+            // (the V buffers start zeroed, every V row stored later is finite
+            // data), and the score MFMAs of the last iterations produce
+            // scores nobody reads.
+            const bool has_sm = j >= 0 && j < wend;
             const int k0 = j * BK;
-            const bool active = (!CAUSAL || k0 <= q0w + 31) && q0w < N;
-            if (active) {
-                // S^T = K Q^T : block mb holds keys k0 + 32 mb + ...
-                f32x16_t s[NMB];
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) {
-                    s[mb] = f32x16_t{};
-                    const int row = 32 * mb + perm_row(li);
-                    const uint8_t* rp = kb + row * (D * 2);
-                    const int sw = swz_k(row);
-#pragma unroll
-                    for (int ks = 0; ks < NS; ++ks) {
-                        const u32x4_t a = *(const u32x4_t*)(rp + (((2 * ks + lh) ^ sw) << 4));
-                        s[mb] = mma<T>(a, qreg[ks], s[mb]);
-                    }
-                }
-                // register r of block mb holds key k0 + 32 mb + 16 (r >> 3) + 8 lh + (r & 7)
+            if (has_sm) {
                 const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
                 if (need_mask) {
+                    // register r of block mb holds key k0 + 8 lh + kk with the
+                    // constant kk below; it is visible iff kk <= lim
+                    int lim = N - 1 - k0 - 8 * lh;
+                    if (CAUSAL) lim = min(lim, qrow - k0 - 8 * lh);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * lh + (r & 7);
-                            const bool hide = (CAUSAL && key > qrow) || key >= N;
-                            if (hide) s[mb][r] = -__builtin_inff();
-                        }
-                }
-                float mx = -__builtin_inff();
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[mb][r]);
-                mx = max_halves(mx);
-                const float mnew = __builtin_fmaxf(m, mx);
-                const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
-                const float mc = mnew * c;
-                m = mnew;
-                float ls = 0.f;
-                u32x4_t pk[2 * NMB];
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * t + 2 * w], c, -mc));
-                            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][8 * t + 2 * w + 1], c, -mc));
-                            ls += p0 + p1;
-                            pk[2 * mb + t][w] = pack2<T>(p0, p1);
-                        }
-                l = l * alpha + ls;
-                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-                }
-                // O^T += V^T P^T : k-step (mb, t) covers keys k0 + 32 mb + 16 t + 8 lh + 0..7
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int d = 32 * db + li;
-                    const uint8_t* rp = vb + d * (BK * 2);
-                    const int sw = swz_v(d);
-#pragma unroll
-                    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const u32x4_t a = *(const u32x4_t*)(rp + (((4 * mb + 2 * t + lh) ^ sw) << 4));
-                            acc[db] = mma<T>(a, pk[2 * mb + t], acc[db]);
+                            const int kk = 32 * mb + 16 * (r >> 3) + (r & 7);
+                            scur[mb][r] = kk > lim ? -__builtin_inff() : scur[mb][r];
                         }
                 }
             }
-            if (j + 1 < jend) lstore(buf ^ 1);
-            __syncthreads();
+            st.live = has_sm;
+            st.mxa = -__builtin_inff();
+            st.mxb = -__builtin_inff();
+            // NSLOT MFMAs, each followed by its share of the softmax;
+            // operands read PD slots ahead
+            u32x4_t opnd[PD + 1];
+#pragma unroll
+            for (int i = 0; i < PD; ++i) opnd[i] = slot_operand(i, kread, vread, ln);
+#pragma unroll
+            for (int i = 0; i < NSLOT; ++i) {
+                if (i + PD < NSLOT) opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
+                slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pprev, qreg);
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    if (group_slot(g) == i) valu_group(g, scur, pcur, st, c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the reference maximum moved: bring the running output to it
+            // (after this iteration's O MFMAs, before the next tile's)
+            if (__builtin_amdgcn_ballot_w64(st.need)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] *= st.alpha;
+            }
+        };
+
+        // the start is hidden from the optimiser so that it does not peel
+        // the first iterations into separately allocated copies of the body
+        int jstart = -1;
+        asm volatile("" : "+s"(jstart));
+#pragma clang loop unroll(disable)
+        for (int j = jstart; j <= jend; j += 2) {
+            iteration(j, BoolTag<true>{});
+            if (j + 1 <= jend) iteration(j + 1, BoolTag<false>{});
         }
 
         // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S))
-        const float lt = sum_halves(l);
+        const float lt = sum_halves(st.l);
         if (q0w < N && qrow < N) {
             const float inv = 1.0f / lt;
             const size_t orow = head_elems + (size_t)qrow * D;
@@ -367,7 +541,7 @@ struct Fwd16 {
                         *(u32x2_t*)((uint16_t*)p.o + orow + d0) = u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)};
                     }
                 }
-            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (m * c + __log2f(lt)) * kLn2;
+            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(lt)) * kLn2;
         }
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
     }
