@@ -33,6 +33,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s at N=4096 d=128 bf16 (causal and non-causal), % MFMA peak"
 KERNEL_SOURCES = ("tiled_exact_attention_fwd_amd/csrc/fa_fwd_kernels.h",
+                  "tiled_exact_attention_fwd_amd/csrc/fa_fwd_launch.h",
+                  "tiled_exact_attention_fwd_amd/csrc/fa_fwd_inst16.hip",
+                  "tiled_exact_attention_fwd_amd/csrc/fa_fwd_inst32.hip",
                   "tiled_exact_attention_fwd_amd/csrc/fa_fwd.hip")
 # the instance bench.py times for the headline (bf16, d=128, non-causal)
 HEADLINE_KERNEL = "fa::BF16, 128, false, false, false"

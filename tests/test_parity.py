@@ -105,6 +105,20 @@ def test_spiky_and_scales(dtype):
     check_against_oracle(words, dtype, True, 2.0, what="large scale")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,scale,values,causal", [(128, 0.5, "normal", False), (64, 1.0, "normal", False),
+                                                   (128, None, "spiky", False)])
+def test_peaked_rows(dtype, d, scale, values, causal):
+    """Softmax rows dominated by one or two keys that first appear after the
+    row's reference was set (several tiles in): the dominant term has to be
+    applied and summed consistently, or its 16-bit rounding shows in O at
+    the 2^-8 level."""
+    words = W.make_words((1, 2, 320, d), dtype, values, seed=d + 7)
+    sc = W.scale_for(d) if scale is None else scale
+    worst, _ = check_against_oracle(words, dtype, causal, sc, what=f"peaked d={d} scale={sc} {values}")
+    print(f"{dtype} peaked d={d} scale={sc} {values}: {worst}")
+
+
 # ---------------------------------------------------------------------------
 # The named workloads at full size, launched as the benchmark launches them;
 # sampled rows against the oracle, properties on every row

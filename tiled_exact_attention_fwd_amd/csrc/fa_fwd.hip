@@ -11,7 +11,7 @@
 #include <cstring>
 
 #include "fa_fwd.h"
-#include "fa_fwd_kernels.h"
+#include "fa_fwd_launch.h"
 
 #ifndef FA_BUILD_FLAGS
 #define FA_BUILD_FLAGS "unknown"
@@ -36,7 +36,7 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 // Default (and only built) tile shape per element type and head dimension.
 void tile_shape(int dtype, int d, int* tq, int* tk) {
     if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
-    else { *tq = 128; *tk = 64; }
+    else { *tq = fa::kTileQ16; *tk = 64; }
 }
 
 int check_args(const fa_fwd_args* a) {
@@ -84,36 +84,6 @@ int check_device() {
     return st == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
 }
 
-template <class K>
-int launch(const FwdParams& p, void* stream) {
-    void* args[] = {const_cast<FwdParams*>(&p)};
-    const hipError_t err = hipLaunchKernel((const void*)&fa::fwd_kernel<K>, dim3(p.total), dim3(K::NT),
-                                          args, 0, (hipStream_t)stream);
-    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-template <class T, int D, bool CAUSAL>
-int pick16(const FwdParams& p, int out_f32, bool count, void* stream) {
-    if (out_f32) {
-        return count ? launch<fa::Fwd16<T, D, CAUSAL, true, true>>(p, stream)
-                     : launch<fa::Fwd16<T, D, CAUSAL, true, false>>(p, stream);
-    }
-    return count ? launch<fa::Fwd16<T, D, CAUSAL, false, true>>(p, stream)
-                 : launch<fa::Fwd16<T, D, CAUSAL, false, false>>(p, stream);
-}
-
-template <class T, int D>
-int pick16c(const FwdParams& p, int causal, int out_f32, bool count, void* stream) {
-    return causal ? pick16<T, D, true>(p, out_f32, count, stream)
-                  : pick16<T, D, false>(p, out_f32, count, stream);
-}
-
-template <int D, bool CAUSAL>
-int pick32(const FwdParams& p, bool count, void* stream) {
-    return count ? launch<fa::Fwd32<D, CAUSAL, true>>(p, stream)
-                 : launch<fa::Fwd32<D, CAUSAL, false>>(p, stream);
-}
-
 int run(const fa_fwd_args* a) {
     int st = check_args(a);
     if (st != FA_OK) return st;
@@ -139,17 +109,20 @@ int run(const fa_fwd_args* a) {
     p.counters = a->counters;
     const bool count = a->counters != nullptr;
 
+    const int c = a->causal, o32 = a->out_dtype;
     switch (a->dtype) {
     case FA_DTYPE_BF16:
-        return a->d == 64 ? pick16c<BF16, 64>(p, a->causal, a->out_dtype, count, a->stream)
-                          : pick16c<BF16, 128>(p, a->causal, a->out_dtype, count, a->stream);
+        if (a->d == 64) return c ? fa::launch16_bf16_d64_c1(p, o32, count, a->stream)
+                                 : fa::launch16_bf16_d64_c0(p, o32, count, a->stream);
+        return c ? fa::launch16_bf16_d128_c1(p, o32, count, a->stream)
+                 : fa::launch16_bf16_d128_c0(p, o32, count, a->stream);
     case FA_DTYPE_F16:
-        return a->d == 64 ? pick16c<F16, 64>(p, a->causal, a->out_dtype, count, a->stream)
-                          : pick16c<F16, 128>(p, a->causal, a->out_dtype, count, a->stream);
+        if (a->d == 64) return c ? fa::launch16_f16_d64_c1(p, o32, count, a->stream)
+                                 : fa::launch16_f16_d64_c0(p, o32, count, a->stream);
+        return c ? fa::launch16_f16_d128_c1(p, o32, count, a->stream)
+                 : fa::launch16_f16_d128_c0(p, o32, count, a->stream);
     default:
-        if (a->d == 64)
-            return a->causal ? pick32<64, true>(p, count, a->stream) : pick32<64, false>(p, count, a->stream);
-        return a->causal ? pick32<128, true>(p, count, a->stream) : pick32<128, false>(p, count, a->stream);
+        return c ? fa::launch32_c1(p, a->d, count, a->stream) : fa::launch32_c0(p, a->d, count, a->stream);
     }
 }
 
@@ -210,7 +183,7 @@ const char* fa_strerror(int status) {
 
 const char* fa_build_info(void) {
     return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
-           "; kernels: bf16/f16 d64 and d128 (128x64 tiles), causal on/off, "
+           "; kernels: bf16/f16 d64 and d128 (128x64 tiles, 32 query rows per wave), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off";
 }
 

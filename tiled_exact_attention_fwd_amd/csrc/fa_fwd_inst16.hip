@@ -1,0 +1,34 @@
+// One 16-bit kernel instance family (element type, head dimension, causal),
+// chosen by FA_INST_T / FA_INST_D / FA_INST_C at compile time: the fp32-output
+// and counter variants of it, and its launcher.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_fwd_launch.h"
+
+#if !defined(FA_INST_T) || !defined(FA_INST_D) || !defined(FA_INST_C)
+#error "FA_INST_T, FA_INST_D and FA_INST_C select the instance"
+#endif
+
+#define FA_CAT6(a, b, c, d, e, f) a##b##c##d##e##f
+#define FA_XCAT6(a, b, c, d, e, f) FA_CAT6(a, b, c, d, e, f)
+#define FA_NAME FA_XCAT6(launch16_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)
+#define FA_TYPE_bf16 BF16
+#define FA_TYPE_f16 F16
+#define FA_TYPE_(t) FA_TYPE_##t
+#define FA_TYPE(t) FA_TYPE_(t)
+
+namespace fa {
+
+int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
+    using T = FA_TYPE(FA_INST_T);
+    constexpr bool C = FA_INST_C != 0;
+    static_assert(Fwd16<T, FA_INST_D, C, false, false>::BQ == kTileQ16, "grid tile");
+    if (out_f32)
+        return count ? launch_kernel<Fwd16<T, FA_INST_D, C, true, true>>(p, stream)
+                     : launch_kernel<Fwd16<T, FA_INST_D, C, true, false>>(p, stream);
+    return count ? launch_kernel<Fwd16<T, FA_INST_D, C, false, true>>(p, stream)
+                 : launch_kernel<Fwd16<T, FA_INST_D, C, false, false>>(p, stream);
+}
+
+}  // namespace fa

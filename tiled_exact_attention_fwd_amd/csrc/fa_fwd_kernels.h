@@ -15,20 +15,19 @@
 //     Each wave owns 32 query rows for the whole key loop.
 //   * The scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 32 key scores of ONE
-//     query, so the row maximum and row sum are in-lane reductions plus one
-//     permlane32 swap between the two half-waves.  The output is also
-//     accumulated transposed, O^T = V^T P^T, so the per-query rescale factor
-//     is a per-lane scalar and P^T feeds the second MFMA straight from
-//     registers (no LDS round trip for P).
+//     query, so the row sums are in-lane reductions plus one permlane32
+//     swap between the two half-waves.  The output is also accumulated
+//     transposed, O^T = V^T P^T, so the per-query rescale factor is a
+//     per-lane scalar and P^T feeds the second MFMA straight from registers
+//     (no LDS round trip for P).
 //   * The key rows of the first MFMA's A operand are loaded in a permuted
 //     order (bits 2 and 3 of the row index swapped) so that each half-wave's
 //     eight consecutive accumulator registers hold eight consecutive keys:
-//     the P^T operand is then a plain register slice and the V^T operand one
-//     16-byte LDS read.
-//   * K and V tiles (tile_k x d, 16 KiB each) are double-buffered in LDS.
-//     Two waves stage K (16-byte coalesced loads, XOR-swizzled rows), two
-//     waves stage V and transpose it to V^T in registers (8x8 blocks) on the
-//     way into LDS.  One barrier per key tile.
+//     the P^T operand is then a plain register slice.
+//   * K and V tiles (tile_k x d, 16 KiB each at d = 128) are double-buffered
+//     in LDS and filled by the buffer unit's direct-to-LDS loads, spread over
+//     the MFMA schedule; V^T operands come from row-major V through the
+//     transposing LDS read.  One barrier per key tile.
 //   * Loads go through buffer resources bounded at the head's extent, so the
 //     ragged last tile reads zeros past row N instead of faulting; those keys
 //     are masked to -inf and those query rows are not stored.
@@ -153,31 +152,46 @@ struct FwdParams {
 // 16-bit kernel (bf16 / fp16)
 //
 // One workgroup = 4 waves = a 128-row query tile of one (batch, head); each
-// wave owns 32 query rows for the whole key loop.  Key tiles are 64 rows.
+// wave owns 32 query rows for the whole key loop; two workgroups share a CU.
+// Key tiles are 64 rows.
 //
 // Per key tile t a wave does three things: the scores S_t = K_t Q^T (16 MFMA
-// at d = 128), the online softmax of S_t (VALU), and O += V_t^T P_t^T (16
-// MFMA).  They are software-pipelined one tile apart, so that iteration j
-// issues the score MFMAs of tile j+1 and the output MFMAs of tile j-1 while
-// the VALU works on the softmax of tile j: the three streams are independent
-// within an iteration, and the MFMAs are interleaved one by one with the
-// softmax instructions (a wave co-issues its own VALU work under a running
-// MFMA).
+// at d = 128), the softmax of S_t (VALU), and O += V_t^T P_t^T (16 MFMA).
+// They are software-pipelined one tile apart, so that iteration j issues the
+// score MFMAs of tile j+1 and the output MFMAs of tile j-1 while the VALU
+// works on the softmax of tile j: the three streams are independent within an
+// iteration, and the MFMAs are interleaved one by one with the softmax
+// instructions (a wave issues its own VALU work under a running MFMA).
 //
 // K and V tiles are copied HBM -> LDS by the buffer unit directly (no VGPR
 // staging), double-buffered: iteration j reads K_{j+1} and V_{j-1} and fills
-// the other halves with K_{j+2} and V_j; one barrier per iteration.  K rows
-// are stored with their 16-byte chunks XOR-swizzled by row so that the
-// 16-byte operand reads of 16 lanes hit distinct banks; V is stored row-major
-// (swizzled the same way for its own access pattern) and read transposed with
-// ds_read_b64_tr_b16, which hands every lane four consecutive keys of one
-// head-dimension column -- the V^T operand of the second product.
+// the other halves with K_{j+2} and V_j, one 16-byte copy per thread every
+// few MFMA slots; one barrier per iteration.  K rows are stored with their
+// 16-byte chunks XOR-swizzled by row so that the 16-byte operand reads of 16
+// lanes hit distinct banks; V is stored row-major (swizzled for its own
+// access pattern) and read transposed with ds_read_b64_tr_b16, which hands
+// every lane four consecutive keys of one head-dimension column -- the V^T
+// operand of the second product.
 //
-// The reference maximum of a row is raised only when a tile's maximum exceeds
-// it by more than 2^8 in the exponent (in units of the base-2 exponent).  Until
-// then the unnormalised terms exp2(c s - c m_ref) stay below 2^8, and the
-// running output and sum need no rescale: the result is the same up to
-// rounding, since numerator and denominator share the reference.
+// Softmax against a reference.  The running maximum of the online softmax
+// only serves to keep the exponentials in range: any per-row reference r
+// gives the same O and log-sum-exp, as long as numerator and denominator
+// share it and no term overflows.  So a row keeps its reference, and its
+// running output unscaled, through every tile whose terms exp2(c s - r) sum
+// to at most 2^15 (which bounds every term and keeps fp16 terms finite) and
+// to at most the row's running sum.  Any other tile -- always the first,
+// whose reference starts at -FLT_MAX -- takes the slow path: the reference
+// is raised to the row's maximum so far, the running output and sum are
+// rescaled by exp2(r_old - r_new), and the tile's terms are recomputed.  The
+// tile maximum is never computed on the fast path.
+//
+// The second condition is for accuracy, not range: the terms are rounded to
+// 16 bits for the output MFMA (relative error up to 2^-8 in bf16) while the
+// sum takes them in fp32.  A term that ends up dominating its row therefore
+// always passes through the slow path, where it becomes exactly 1 (or a
+// power of two after later rescales) and is rounded without error; a term
+// that never triggers the slow path is at most the running sum before it,
+// hence at most half of the row's final sum.
 // ---------------------------------------------------------------------------
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -188,25 +202,28 @@ __device__ __forceinline__ u32x2_t lds_read_tr(const uint8_t* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-// max(a, b, c) in one instruction (no NaN canonicalisation of the inputs)
-__device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
 // keeps a value's computation at this point of the instruction stream: the
 // compiler may not sink it past here (the MFMA interleave depends on it)
 template <class X> __device__ __forceinline__ void pin(X& x) { asm volatile("" : "+v"(x)); }
 
-constexpr float kRescaleThreshold = 8.0f;
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+template <int I> struct IntTag { static constexpr int value = I; };
 
-template <bool B> struct BoolTag { static constexpr bool value = B; };   // log2 of the largest unnormalised term
+// f(IntTag<I>{}) for I = B .. E-1, unrolled by construction (the loop bodies
+// here are too large for the optimiser's unroll limits)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntTag<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT>
 struct Fwd16 {
-    static constexpr int BQ = 128;                 // query rows per workgroup
     static constexpr int WAVES = 4;
-    static constexpr int OCC = 2;                  // waves per SIMD (<= 256 registers each)
+    static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
+    static constexpr int OCC = 2;                  // workgroups per CU
     static constexpr int NT = 64 * WAVES;
     static constexpr int BK = 64;                  // keys per tile
     static constexpr int ROWB = 2 * D;             // bytes per K / V row
@@ -217,10 +234,10 @@ struct Fwd16 {
     static constexpr int NKS = BK / 16;            // k-steps of V^T P^T per tile
     static constexpr int NPV = NDB * NKS;          // output MFMAs per tile
     static constexpr int NQK = NMB * NS;           // score MFMAs per tile
-    static constexpr int NSLOT = NPV + NQK;
+    static constexpr int NSLOT = NPV + NQK;        // one MFMA per slot
     static constexpr int NV = BK / 2;              // scores per lane per tile
     static constexpr int LOADS = TILEB / (NT * 16);// 16-byte copies per thread per tile
-    static constexpr int PD = 3;                   // operand prefetch distance (MFMA slots)
+    static constexpr int PD = 3;                   // operand prefetch distance (slots)
     static constexpr int LDS = 4 * TILEB;
     static_assert(D == 64 || D == 128, "head dimension");
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile copy");
@@ -250,20 +267,17 @@ struct Fwd16 {
         const int chunk = pos ^ (ISK ? fk(row) : fv(row));
         return (uint32_t)(row * ROWB + chunk * 16);
     }
-    // One tile HBM -> LDS; every thread issues LOADS 16-byte copies.  The
-    // whole offset goes in the VGPR operand: the buffer unit range-checks
-    // that one against the head's extent (reads past row N return zero), so
-    // no part of it may be moved to the scalar offset.
-    static __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, int k0,
-                                                     int wave, uint32_t src) {
-#pragma unroll
-        for (int u = 0; u < LOADS; ++u) {
-            const int blk = u * WAVES + wave;             // 1 KiB block of the tile
-            uint32_t off = src + (uint32_t)(k0 * ROWB + u * WAVES * 1024);
-            asm volatile("" : "+v"(off));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(lbuf + blk * 1024), 16, off, 0, 0, 0);
-        }
+    // The u-th of a thread's LOADS 16-byte copies of one tile HBM -> LDS.
+    // The whole offset goes in the VGPR operand: the buffer unit
+    // range-checks that one against the head's extent (reads past row N
+    // return zero), so no part of it may be moved to the scalar offset.
+    static __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, int k0,
+                                                     int wave, uint32_t src, int u) {
+        const int blk = u * WAVES + wave;              // 1 KiB block of the tile
+        uint32_t off = src + (uint32_t)(k0 * ROWB + u * WAVES * 1024);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lbuf + blk * 1024), 16, off, 0, 0, 0);
     }
 
     static __device__ __forceinline__ u32x4_t k_operand(const uint8_t* kb, const Lane& ln, int mb, int ks) {
@@ -275,8 +289,8 @@ struct Fwd16 {
         return u32x4_t{a[0], a[1], b[0], b[1]};
     }
 
-    // the MFMA of one slot: slots [0, NPV) are O^T += V^T P^T (k-step major, so
-    // consecutive MFMAs go to different accumulators), the rest S^T = K Q^T
+    // The MFMA of slot i: slots [0, NPV) are O^T += V^T P^T (k-step major, so
+    // consecutive slots go to different accumulators), the rest S^T = K Q^T.
     static __device__ __forceinline__ void slot_mfma(int i, u32x4_t a, f32x16_t* acc, f32x16_t* snext,
                                                      const u32x4_t* pprev, const u32x4_t* qreg) {
         if (i < NPV) {
@@ -297,63 +311,94 @@ struct Fwd16 {
     // softmax state of one lane (one query row; both half-waves hold it)
     struct Soft {
         float mc;      // reference maximum times c (base-2 exponent units)
-        float l;       // running sum of this half-wave's terms
-        float alpha;   // rescale factor of the current tile
-        float mxa, mxb;
+        float l;       // running sum of the row's terms (previous tiles, both halves)
+        float lt;      // this tile's sum of this half-wave's terms
         float meff;    // mc, or +inf when this iteration has no tile (terms are 0)
-        bool need;
-        bool live;     // this iteration has a tile of this wave
     };
 
-    // VALU work of the softmax, split into groups spread over the MFMA slots:
-    // groups [0, NV/2) fold two scores into the row maximum, group NV/2 makes
-    // the new reference and the correction, groups after it turn two scores
-    // into two terms, round them to 16 bits, pack them and add them to l.
-    static constexpr int NG = NV / 2 + 1 + NV / 2;
-    static constexpr int cost(int g) { return g < NV / 2 ? 1 : (g == NV / 2 ? 8 : 7); }
-    static constexpr int cum(int g) { return g == 0 ? 0 : cum(g - 1) + cost(g - 1); }
-    static constexpr int group_slot(int g) { return cum(g) * NSLOT / cum(NG); }
-    // the term registers of k-step kt are rewritten only after the last
-    // output MFMA that reads them (slot kt * NDB + NDB - 1)
+    // The softmax of a tile turns each score s into the term
+    // exp2(c s - mc) against the row's reference mc, in three stages one or
+    // two MFMA slots apart (so no instruction waits on the one before it):
+    //   A  x = c s - mc for two scores                      (2 fma)
+    //   B  p = 2^x                                          (2 exp)
+    //   C  pack the two terms to 16 bits, add them to the tile sum
+    //                                                       (cvt, 2 add)
+    // Pair k (scores 2k, 2k+1) starts at slot pair_slot(k).  Its stage C
+    // rewrites the term registers of k-step k/4, which the output MFMAs of
+    // slots [NDB (k/4), NDB (k/4 + 1)) read first.
+    static constexpr int NPAIR = NV / 2;
+    static constexpr int DB_ = D == 128 ? 1 : 0;     // stage B delay (slots)
+    static constexpr int DC_ = D == 128 ? 2 : 1;     // stage C delay (slots)
+    static constexpr int P_FIRST = D == 128 ? 2 : 1;
+    static constexpr int P_LAST = NSLOT - 1 - DC_;
+    static constexpr int pair_slot(int k) { return P_FIRST + ((P_LAST - P_FIRST) * k) / (NPAIR - 1); }
     static constexpr bool terms_after_reads() {
-        for (int k = 0; k < NV / 2; ++k)
-            if (group_slot(NV / 2 + 1 + k) <= (k / 4) * NDB + NDB - 1) return false;
+        for (int k = 0; k < NPAIR; ++k)
+            if (pair_slot(k) + DC_ < (k / 4) * NDB + NDB) return false;
         return true;
     }
     static_assert(terms_after_reads(), "softmax would overwrite terms before the output MFMA reads them");
+    // copies of the next tiles: one 16-byte copy every COPY_EVERY slots
+    static constexpr int NCOPY = 2 * LOADS;
+    static constexpr int COPY_EVERY = NSLOT / NCOPY;
+    static_assert(COPY_EVERY >= 1 && NCOPY * COPY_EVERY <= NSLOT, "copy spread");
 
-    static __device__ __forceinline__ void valu_group(int g, const f32x16_t* scur, u32x4_t* pcur,
-                                                      Soft& st, float c) {
-        auto val = [&](int v) { return scur[v / 16][v % 16]; };
-        if (g < NV / 2) {
-            float& m = (g & 1) ? st.mxb : st.mxa;
-            m = max3(m, val(2 * g), val(2 * g + 1));
-        } else if (g == NV / 2) {
-            float mx;
-            asm volatile("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(st.mxa), "v"(st.mxb));
-            mx = max_halves(mx);
-            const float mxc = mx * c;
-            st.need = st.live && mxc > st.mc + kRescaleThreshold;
-            const float nmc = st.need ? mxc : st.mc;
-            st.alpha = st.need ? __builtin_amdgcn_exp2f(st.mc - nmc) : 1.0f;
-            st.mc = nmc;
-            st.meff = st.live ? nmc : __builtin_inff();
-            st.l *= st.alpha;
-            pin(st.meff);
-            pin(st.l);
-        } else {
-            const int k = g - NV / 2 - 1;   // pair index: scores 2k, 2k+1
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(val(2 * k), c, -st.meff));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(val(2 * k + 1), c, -st.meff));
-            // the sum takes the fp32 terms: the log-sum-exp has to hold to
-            // 1e-3, which the 16-bit rounding of a dominant term would not
-            uint32_t pk = pack2<T>(p0, p1);
-            st.l += p0;
-            st.l += p1;
-            pin(pk);
-            pin(st.l);
-            pcur[k / 4][k % 4] = pk;
+    // a tile whose terms sum to more than this (the sum bounds every term)
+    // takes the slow path; fp16 holds terms up to 65504
+    static constexpr float kTileSumLimit = 32768.0f;
+
+    static __device__ __forceinline__ void stage_a(const f32x16_t* scur, int k, const Soft& st, float c,
+                                                   float& x0, float& x1) {
+        x0 = __builtin_fmaf(scur[(2 * k) / 16][(2 * k) % 16], c, -st.meff);
+        x1 = __builtin_fmaf(scur[(2 * k + 1) / 16][(2 * k + 1) % 16], c, -st.meff);
+        pin(x0);
+        pin(x1);
+    }
+    static __device__ __forceinline__ void stage_b(float& x0, float& x1) {
+        x0 = __builtin_amdgcn_exp2f(x0);
+        x1 = __builtin_amdgcn_exp2f(x1);
+        pin(x0);
+        pin(x1);
+    }
+    static __device__ __forceinline__ void stage_c(u32x4_t* pcur, int k, Soft& st, float x0, float x1) {
+        uint32_t w = pack2<T>(x0, x1);
+        st.lt += x0;
+        st.lt += x1;
+        pin(w);
+        pin(st.lt);
+        pcur[k / 4][k % 4] = w;
+    }
+
+    // Slow path of a tile: lanes that need it raise their reference to the
+    // larger of it and the tile's maximum; the running output and sum are
+    // rescaled by the correction exp2(old - new) and the tile's terms and sum
+    // are recomputed.  Other lanes keep their reference and terms (their
+    // correction is 1).
+    static __device__ void raise_reference(const f32x16_t* scur, u32x4_t* pcur, Soft& st, float c,
+                                           f32x16_t* acc, bool need) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, scur[mb][r]);
+        mx = max_halves(mx);
+        const float nmc = need ? __builtin_fmaxf(st.mc, mx * c) : st.mc;
+        const float alpha = __builtin_amdgcn_exp2f(st.mc - nmc);
+        st.mc = nmc;
+        st.meff = nmc;
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        float lt = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPAIR; ++k) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[(2 * k) / 16][(2 * k) % 16], c, -nmc));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[(2 * k + 1) / 16][(2 * k + 1) % 16], c, -nmc));
+            const uint32_t w = pack2<T>(p0, p1);
+            if (need) pcur[k / 4][k % 4] = w;
+            lt += p0 + p1;
         }
+        if (need) st.lt = lt;
     }
 
     static __device__ void run(const FwdParams& p) {
@@ -372,7 +417,7 @@ struct Fwd16 {
         int qi = L - hh * p.tiles_q;
         if (CAUSAL) qi = p.tiles_q - 1 - qi;
         const int qt0 = qi * BQ;
-        const int q0w = qt0 + wave * 32;
+        const int q0w = qt0 + wave * 32;            // first row of this wave; lane li holds row q0w + li
         const int qrow = q0w + li;
 
         const size_t head_elems = (size_t)hh * N * D;
@@ -382,7 +427,10 @@ struct Fwd16 {
         const auto rv = make_rsrc((const uint8_t*)p.v + head_elems * 2, head_bytes);
 
         const int nk = (N + BK - 1) / BK;
-        const int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        // opaque to the optimiser: reasoning about the causal bound makes it
+        // allocate the loop body with more registers than the CU holds
+        asm volatile("" : "+s"(jend));
         // key tiles this wave computes (all of them, up to its diagonal when causal)
         int wend = q0w < N ? (CAUSAL ? min(jend, (q0w + 31) / BK + 1) : jend) : 0;
         wend = __builtin_amdgcn_readfirstlane(wend);
@@ -399,7 +447,7 @@ struct Fwd16 {
             ((u32x4_t*)kbuf1)[i] = u32x4_t{0, 0, 0, 0};
         }
 
-        // Q^T operand: lane (li, lh) holds Q[qrow][16 s + 8 lh .. +7]
+        // Q^T operand: lane (li, lh) holds Q[row][16 s + 8 lh .. +7]
         u32x4_t qreg[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -422,30 +470,32 @@ struct Fwd16 {
         }
 
         f32x16_t acc[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
         f32x16_t s0[NMB], s1[NMB];     // scores of even / odd tiles
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) s0[mb] = s1[mb] = f32x16_t{};
         // packed terms: the output MFMAs of an iteration read the previous
         // tile's terms from the same registers the softmax then overwrites
         // with this tile's (each k-step's registers only after their last read)
         u32x4_t pk[NKS];
+        Soft st;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) s0[mb] = s1[mb] = f32x16_t{};
 #pragma unroll
         for (int kt = 0; kt < NKS; ++kt) pk[kt] = u32x4_t{0, 0, 0, 0};
-        Soft st;
-        st.mc = -__builtin_inff();
-        st.l = 0.f;
-        st.alpha = 1.f;
+        // the first tile's terms overflow against this reference, which sends
+        // it through the slow path that sets the real one
+        st.mc = -__FLT_MAX__;
+        st.l = st.lt = 0.f;
         const float c = p.c;
 
         const uint32_t ksrc = copy_offset<true>(wave, lane);
         const uint32_t vsrc = copy_offset<false>(wave, lane);
 
         // prologue: K_0 into kbuf0
-        copy_tile(rk, kbuf0, 0, wave, ksrc);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) copy_part(rk, kbuf0, 0, wave, ksrc, u);
 
-        // iteration j (see the header comment); ODD selects the buffers / arrays
+        // iteration j (see the section comment); ODD selects the buffers / arrays
         auto iteration = [&](const int j, auto odd_tag) {
             constexpr bool ODD = decltype(odd_tag)::value;
             uint8_t* kread = ODD ? kbuf0 : kbuf1;      // K_{j+1}
@@ -454,22 +504,17 @@ struct Fwd16 {
             uint8_t* vfill = ODD ? vbuf1 : vbuf0;      // V_j
             f32x16_t* scur = ODD ? s1 : s0;
             f32x16_t* snext = ODD ? s0 : s1;
-            u32x4_t* pprev = pk;
-            u32x4_t* pcur = pk;
 
             __syncthreads();   // this wave's copies done (vmcnt 0), and everyone's
-            if (j + 2 < jend) copy_tile(rk, kfill, (j + 2) * BK, wave, ksrc);
-            if (j >= 0 && j < jend) copy_tile(rv, vfill, j * BK, wave, vsrc);
 
             // Every iteration runs the same straight-line schedule (one
             // register allocation, no divergent code paths).  Where a stream
             // has nothing to do its work is made harmless instead of skipped:
-            // the softmax of an iteration without a tile of this wave sees
-            // need = false and a reference of +inf, so its terms are exactly 0
-            // and its state is unchanged; the output MFMAs then add 0 * V
-            // (the V buffers start zeroed, every V row stored later is finite
-            // data), and the score MFMAs of the last iterations produce
-            // scores nobody reads.
+            // the softmax of an iteration without a tile of this wave uses a
+            // reference of +inf, so its terms and sums are exactly 0; the
+            // output MFMAs then add 0 * V (the V buffers start zeroed, every V
+            // row stored later is finite data), and the score MFMAs of the
+            // last iterations produce scores nobody reads.
             const bool has_sm = j >= 0 && j < wend;
             const int k0 = j * BK;
             if (has_sm) {
@@ -488,29 +533,46 @@ struct Fwd16 {
                         }
                 }
             }
-            st.live = has_sm;
-            st.mxa = -__builtin_inff();
-            st.mxb = -__builtin_inff();
-            // NSLOT MFMAs, each followed by its share of the softmax;
-            // operands read PD slots ahead
+            st.meff = has_sm ? st.mc : __builtin_inff();
+            st.lt = 0.f;
+
+            // NSLOT slots; in each: its MFMA and its share of the softmax
+            // stages, then the LDS operand read of slot i + PD; one 16-byte
+            // copy of the next tiles every COPY_EVERY slots
+            float xs[NPAIR][2];
             u32x4_t opnd[PD + 1];
-#pragma unroll
-            for (int i = 0; i < PD; ++i) opnd[i] = slot_operand(i, kread, vread, ln);
-#pragma unroll
-            for (int i = 0; i < NSLOT; ++i) {
-                if (i + PD < NSLOT) opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
-                slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pprev, qreg);
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    if (group_slot(g) == i) valu_group(g, scur, pcur, st, c);
+            static_for<0, PD>([&](auto I) { opnd[I.value] = slot_operand(I.value, kread, vread, ln); });
+            static_for<0, NSLOT>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i % COPY_EVERY == 1 % COPY_EVERY && i / COPY_EVERY < NCOPY) {
+                    constexpr int cu = i / COPY_EVERY;
+                    if constexpr (cu < LOADS) {
+                        if (j + 2 < jend) copy_part(rk, kfill, (j + 2) * BK, wave, ksrc, cu);
+                    } else {
+                        if (j >= 0 && j < jend) copy_part(rv, vfill, j * BK, wave, vsrc, cu - LOADS);
+                    }
+                }
+                slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pk, qreg);
+                static_for<0, NPAIR>([&](auto K) {
+                    constexpr int k = decltype(K)::value;
+                    if constexpr (pair_slot(k) == i) stage_a(scur, k, st, c, xs[k][0], xs[k][1]);
+                    if constexpr (pair_slot(k) + DB_ == i) stage_b(xs[k][0], xs[k][1]);
+                    if constexpr (pair_slot(k) + DC_ == i) stage_c(pk, k, st, xs[k][0], xs[k][1]);
+                });
+                if constexpr (i + PD < NSLOT) opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
                 __builtin_amdgcn_sched_barrier(0);
+            });
+
+            // the tile's sum decides the slow path (reference raised, running
+            // output rescaled after this iteration's output MFMAs and before
+            // the next tile's); then the tile joins the running sum
+            float lt = sum_halves(st.lt);
+            const bool need = lt > kTileSumLimit || lt > st.l;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                raise_reference(scur, pk, st, c, acc, need);
+                lt = sum_halves(st.lt);
             }
-            // the reference maximum moved: bring the running output to it
-            // (after this iteration's O MFMAs, before the next tile's)
-            if (__builtin_amdgcn_ballot_w64(st.need)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] *= st.alpha;
-            }
+            st.l += lt;
         };
 
         // the start is hidden from the optimiser so that it does not peel
@@ -523,10 +585,10 @@ struct Fwd16 {
             if (j + 1 <= jend) iteration(j + 1, BoolTag<false>{});
         }
 
-        // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S))
-        const float lt = sum_halves(st.l);
-        if (q0w < N && qrow < N) {
-            const float inv = 1.0f / lt;
+        // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S)) = (mc + log2 l) ln 2
+        const float l = st.l;
+        if (qrow < N) {
+            const float inv = 1.0f / l;
             const size_t orow = head_elems + (size_t)qrow * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -541,12 +603,11 @@ struct Fwd16 {
                         *(u32x2_t*)((uint16_t*)p.o + orow + d0) = u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)};
                     }
                 }
-            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(lt)) * kLn2;
+            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
         }
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
     }
 };
-
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 MFMA (v_mfma_f32_32x32x2_f32), 64 x 64 tiles
 // ---------------------------------------------------------------------------

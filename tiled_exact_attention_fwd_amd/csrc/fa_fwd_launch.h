@@ -1,0 +1,39 @@
+// Kernel-instance launchers of the forward library.  Each is defined in its
+// own translation unit (fa_fwd_inst16.hip / fa_fwd_inst32.hip compiled once
+// per instance) so the instances build in parallel; the host layer
+// (fa_fwd.hip) picks one after its argument checks.  All return an fa_status.
+#pragma once
+
+#include "fa_fwd.h"
+#include "fa_fwd_kernels.h"
+
+namespace fa {
+
+// Query rows per workgroup of the 16-bit kernels (4 waves x 32 rows); the
+// host sizes the grid with it.
+constexpr int kTileQ16 = 128;
+
+#define FA_DECLARE16(T, D, C) \
+    int launch16_##T##_d##D##_c##C(const FwdParams& p, int out_f32, bool count, void* stream);
+FA_DECLARE16(bf16, 64, 0)
+FA_DECLARE16(bf16, 64, 1)
+FA_DECLARE16(bf16, 128, 0)
+FA_DECLARE16(bf16, 128, 1)
+FA_DECLARE16(f16, 64, 0)
+FA_DECLARE16(f16, 64, 1)
+FA_DECLARE16(f16, 128, 0)
+FA_DECLARE16(f16, 128, 1)
+#undef FA_DECLARE16
+int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
+int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
+
+// launch of one kernel instance on the caller's stream
+template <class K>
+int launch_kernel(const FwdParams& p, void* stream) {
+    void* args[] = {const_cast<FwdParams*>(&p)};
+    const hipError_t err = hipLaunchKernel((const void*)&fwd_kernel<K>, dim3(p.total), dim3(K::NT),
+                                          args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa
