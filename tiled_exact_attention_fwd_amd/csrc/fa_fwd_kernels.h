@@ -267,14 +267,17 @@ struct Fwd16 {
         const int chunk = pos ^ (ISK ? fk(row) : fv(row));
         return (uint32_t)(row * ROWB + chunk * 16);
     }
-    // The u-th of a thread's LOADS 16-byte copies of one tile HBM -> LDS.
-    // The whole offset goes in the VGPR operand: the buffer unit
-    // range-checks that one against the head's extent (reads past row N
-    // return zero), so no part of it may be moved to the scalar offset.
-    static __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, int k0,
+    // The u-th of a thread's LOADS 16-byte copies of one tile HBM -> LDS;
+    // tile_off is the tile's byte offset in the head, or the head's extent
+    // for a copy that must not fetch anything.  The whole offset goes in the
+    // VGPR operand: the buffer unit range-checks that one against the head's
+    // extent (reads past row N return zero), so no part of it may be moved
+    // to the scalar offset.  Extents stay below 2^30 bytes, so the sum
+    // cannot wrap into range.
+    static __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, uint32_t tile_off,
                                                      int wave, uint32_t src, int u) {
         const int blk = u * WAVES + wave;              // 1 KiB block of the tile
-        uint32_t off = src + (uint32_t)(k0 * ROWB + u * WAVES * 1024);
+        uint32_t off = src + tile_off + (uint32_t)(u * WAVES * 1024);
         asm volatile("" : "+v"(off));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             r, (__attribute__((address_space(3))) void*)(lbuf + blk * 1024), 16, off, 0, 0, 0);
@@ -493,7 +496,7 @@ struct Fwd16 {
 
         // prologue: K_0 into kbuf0
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) copy_part(rk, kbuf0, 0, wave, ksrc, u);
+        for (int u = 0; u < LOADS; ++u) copy_part(rk, kbuf0, 0u, wave, ksrc, u);
 
         // iteration j (see the section comment); ODD selects the buffers / arrays
         auto iteration = [&](const int j, auto odd_tag) {
@@ -535,6 +538,12 @@ struct Fwd16 {
             }
             st.meff = has_sm ? st.mc : __builtin_inff();
             st.lt = 0.f;
+            // the copies of this iteration (K_{j+2}, V_j) are issued without
+            // branches: a tile outside [0, jend) is pointed past the head's
+            // end and reads as zeros, into a buffer nobody reads before it is
+            // filled again (K) or that is multiplied by zero terms (V)
+            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : head_bytes;
+            const uint32_t vcopy = j >= 0 && j < jend ? (uint32_t)(j * TILEB) : head_bytes;
 
             // NSLOT slots; in each: its MFMA and its share of the softmax
             // stages, then the LDS operand read of slot i + PD; one 16-byte
@@ -546,11 +555,8 @@ struct Fwd16 {
                 constexpr int i = decltype(I)::value;
                 if constexpr (i % COPY_EVERY == 1 % COPY_EVERY && i / COPY_EVERY < NCOPY) {
                     constexpr int cu = i / COPY_EVERY;
-                    if constexpr (cu < LOADS) {
-                        if (j + 2 < jend) copy_part(rk, kfill, (j + 2) * BK, wave, ksrc, cu);
-                    } else {
-                        if (j >= 0 && j < jend) copy_part(rv, vfill, j * BK, wave, vsrc, cu - LOADS);
-                    }
+                    if constexpr (cu < LOADS) copy_part(rk, kfill, kcopy, wave, ksrc, cu);
+                    else copy_part(rv, vfill, vcopy, wave, vsrc, cu - LOADS);
                 }
                 slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pk, qreg);
                 static_for<0, NPAIR>([&](auto K) {
