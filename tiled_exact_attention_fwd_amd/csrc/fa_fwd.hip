@@ -33,10 +33,10 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Default (and only built) tile shape per element type and head dimension.
-void tile_shape(int dtype, int d, int* tq, int* tk) {
+// Default (and only built) tile shape per element type, head dimension and mask.
+void tile_shape(int dtype, int d, int causal, int* tq, int* tk) {
     if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
-    else { *tq = fa::kTileQ16; *tk = 64; }
+    else { *tq = fa::tile_q16(causal != 0); *tk = 64; }
 }
 
 int check_args(const fa_fwd_args* a) {
@@ -50,7 +50,7 @@ int check_args(const fa_fwd_args* a) {
         return FA_ERR_UNSUPPORTED;
     if (a->d != 64 && a->d != 128) return FA_ERR_UNSUPPORTED;
     int tq, tk;
-    tile_shape(a->dtype, a->d, &tq, &tk);
+    tile_shape(a->dtype, a->d, a->causal, &tq, &tk);
     if (a->tile_q < 0 || a->tile_k < 0) return FA_ERR_INVALID;
     if ((a->tile_q && a->tile_q != tq) || (a->tile_k && a->tile_k != tk)) return FA_ERR_UNSUPPORTED;
     const int e = elem_size(a->dtype);
@@ -91,7 +91,7 @@ int run(const fa_fwd_args* a) {
     if (st != FA_OK) return st;
 
     int tq, tk;
-    tile_shape(a->dtype, a->d, &tq, &tk);
+    tile_shape(a->dtype, a->d, a->causal, &tq, &tk);
     FwdParams p;
     p.q = a->q;
     p.k = a->k;
@@ -167,7 +167,7 @@ int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k) {
     if (!tile_q || !tile_k || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    tile_shape(dtype, d, tile_q, tile_k);
+    tile_shape(dtype, d, causal, tile_q, tile_k);
     return FA_OK;
 }
 
@@ -183,7 +183,7 @@ const char* fa_strerror(int status) {
 
 const char* fa_build_info(void) {
     return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
-           "; kernels: bf16/f16 d64 and d128 (128x64 tiles, 32 query rows per wave), causal on/off, "
+           "; kernels: bf16/f16 d64 and d128 (256x64 tiles non-causal, 128x64 causal, 32 query rows per wave), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off";
 }
 

@@ -23,7 +23,7 @@ namespace fa {
 int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
     using T = FA_TYPE(FA_INST_T);
     constexpr bool C = FA_INST_C != 0;
-    static_assert(Fwd16<T, FA_INST_D, C, false, false>::BQ == kTileQ16, "grid tile");
+    static_assert(Fwd16<T, FA_INST_D, C, true, true>::BQ == tile_q16(C), "grid tile");
     if (out_f32)
         return count ? launch_kernel<Fwd16<T, FA_INST_D, C, true, true>>(p, stream)
                      : launch_kernel<Fwd16<T, FA_INST_D, C, true, false>>(p, stream);

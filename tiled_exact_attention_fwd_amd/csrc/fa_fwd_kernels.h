@@ -221,9 +221,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT>
 struct Fwd16 {
-    static constexpr int WAVES = 4;
+    // Eight waves (256 query rows, one workgroup per CU) share each K / V
+    // tile copy without a mask: half the L2 -> LDS traffic of four.  Causal
+    // launches keep four waves (128 rows, two workgroups per CU): their
+    // waves' work differs along the diagonal, and a smaller workgroup waits
+    // less at its barriers for the wave with the most keys.
+    static constexpr int WAVES = CAUSAL ? 4 : 8;
     static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
-    static constexpr int OCC = 2;                  // workgroups per CU
+    static constexpr int OCC = 2;                  // waves per SIMD
     static constexpr int NT = 64 * WAVES;
     static constexpr int BK = 64;                  // keys per tile
     static constexpr int ROWB = 2 * D;             // bytes per K / V row
@@ -267,18 +272,15 @@ struct Fwd16 {
         const int chunk = pos ^ (ISK ? fk(row) : fv(row));
         return (uint32_t)(row * ROWB + chunk * 16);
     }
-    // The u-th of a thread's LOADS 16-byte copies of one tile HBM -> LDS;
-    // tile_off is the tile's byte offset in the head, or the head's extent
-    // for a copy that must not fetch anything.  The whole offset goes in the
-    // VGPR operand: the buffer unit range-checks that one against the head's
-    // extent (reads past row N return zero), so no part of it may be moved
-    // to the scalar offset.  Extents stay below 2^30 bytes, so the sum
-    // cannot wrap into range.
-    static __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, uint32_t tile_off,
-                                                     int wave, uint32_t src, int u) {
+    // The u-th of a thread's LOADS 16-byte copies of one tile HBM -> LDS.
+    // r is a buffer resource based at the tile's first row whose extent is
+    // what is left of the head from there (zero for a tile past the end);
+    // off is the thread's byte offset inside the tile.  The buffer unit
+    // range-checks the VGPR offset against that extent, so rows past N read
+    // as zeros.
+    static __device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t r, uint8_t* lbuf, int wave,
+                                                     uint32_t off, int u) {
         const int blk = u * WAVES + wave;              // 1 KiB block of the tile
-        uint32_t off = src + tile_off + (uint32_t)(u * WAVES * 1024);
-        asm volatile("" : "+v"(off));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             r, (__attribute__((address_space(3))) void*)(lbuf + blk * 1024), 16, off, 0, 0, 0);
     }
@@ -426,8 +428,8 @@ struct Fwd16 {
         const size_t head_elems = (size_t)hh * N * D;
         const uint32_t head_bytes = (uint32_t)N * ROWB;
         const auto rq = make_rsrc((const uint8_t*)p.q + head_elems * 2, head_bytes);
-        const auto rk = make_rsrc((const uint8_t*)p.k + head_elems * 2, head_bytes);
-        const auto rv = make_rsrc((const uint8_t*)p.v + head_elems * 2, head_bytes);
+        const uint8_t* kbase = (const uint8_t*)p.k + head_elems * 2;
+        const uint8_t* vbase = (const uint8_t*)p.v + head_elems * 2;
 
         const int nk = (N + BK - 1) / BK;
         int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
@@ -491,12 +493,22 @@ struct Fwd16 {
         st.l = st.lt = 0.f;
         const float c = p.c;
 
+        // this thread's byte offsets inside a K / V tile, one per copy
         const uint32_t ksrc = copy_offset<true>(wave, lane);
         const uint32_t vsrc = copy_offset<false>(wave, lane);
+        uint32_t koff_c[LOADS], voff_c[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            koff_c[u] = ksrc + (uint32_t)(u * WAVES * 1024);
+            voff_c[u] = vsrc + (uint32_t)(u * WAVES * 1024);
+        }
 
         // prologue: K_0 into kbuf0
+        {
+            const auto rk0 = make_rsrc(kbase, head_bytes);
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) copy_part(rk, kbuf0, 0u, wave, ksrc, u);
+            for (int u = 0; u < LOADS; ++u) copy_part(rk0, kbuf0, wave, koff_c[u], u);
+        }
 
         // iteration j (see the section comment); ODD selects the buffers / arrays
         auto iteration = [&](const int j, auto odd_tag) {
@@ -539,11 +551,14 @@ struct Fwd16 {
             st.meff = has_sm ? st.mc : __builtin_inff();
             st.lt = 0.f;
             // the copies of this iteration (K_{j+2}, V_j) are issued without
-            // branches: a tile outside [0, jend) is pointed past the head's
-            // end and reads as zeros, into a buffer nobody reads before it is
-            // filled again (K) or that is multiplied by zero terms (V)
+            // branches: a tile outside [0, jend) is given an empty extent and
+            // reads as zeros, into a buffer nobody reads before it is filled
+            // again (K) or that is multiplied by zero terms (V).  Extents stay
+            // below 2^30 bytes (host check), so these sums cannot wrap.
             const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : head_bytes;
             const uint32_t vcopy = j >= 0 && j < jend ? (uint32_t)(j * TILEB) : head_bytes;
+            const auto rkt = make_rsrc(kbase + kcopy, head_bytes - kcopy);
+            const auto rvt = make_rsrc(vbase + vcopy, head_bytes - vcopy);
 
             // NSLOT slots; in each: its MFMA and its share of the softmax
             // stages, then the LDS operand read of slot i + PD; one 16-byte
@@ -555,8 +570,8 @@ struct Fwd16 {
                 constexpr int i = decltype(I)::value;
                 if constexpr (i % COPY_EVERY == 1 % COPY_EVERY && i / COPY_EVERY < NCOPY) {
                     constexpr int cu = i / COPY_EVERY;
-                    if constexpr (cu < LOADS) copy_part(rk, kfill, kcopy, wave, ksrc, cu);
-                    else copy_part(rv, vfill, vcopy, wave, vsrc, cu - LOADS);
+                    if constexpr (cu < LOADS) copy_part(rkt, kfill, wave, koff_c[cu], cu);
+                    else copy_part(rvt, vfill, wave, voff_c[cu - LOADS], cu - LOADS);
                 }
                 slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pk, qreg);
                 static_for<0, NPAIR>([&](auto K) {
@@ -585,10 +600,30 @@ struct Fwd16 {
         // the first iterations into separately allocated copies of the body
         int jstart = -1;
         asm volatile("" : "+s"(jstart));
+        // iterations up to j = wend carry this wave's work (its last output
+        // MFMAs run at j = wend); after that, up to jend, it only keeps up its
+        // share of the workgroup's barriers and copies
+        const int jlast = min(jend, wend);
 #pragma clang loop unroll(disable)
-        for (int j = jstart; j <= jend; j += 2) {
+        for (int j = jstart; j <= jlast; j += 2) {
             iteration(j, BoolTag<true>{});
-            if (j + 1 <= jend) iteration(j + 1, BoolTag<false>{});
+            if (j + 1 <= jlast) iteration(j + 1, BoolTag<false>{});
+        }
+#pragma clang loop unroll(disable)
+        for (int j = jlast + 1; j <= jend; ++j) {
+            __syncthreads();
+            const bool odd = j & 1;
+            uint8_t* kfill = odd ? kbuf1 : kbuf0;
+            uint8_t* vfill = odd ? vbuf1 : vbuf0;
+            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : head_bytes;
+            const uint32_t vcopy = j < jend ? (uint32_t)(j * TILEB) : head_bytes;
+            const auto rkt = make_rsrc(kbase + kcopy, head_bytes - kcopy);
+            const auto rvt = make_rsrc(vbase + vcopy, head_bytes - vcopy);
+#pragma unroll
+            for (int u = 0; u < LOADS; ++u) {
+                copy_part(rkt, kfill, wave, koff_c[u], u);
+                copy_part(rvt, vfill, wave, voff_c[u], u);
+            }
         }
 
         // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S)) = (mc + log2 l) ln 2
@@ -614,6 +649,7 @@ struct Fwd16 {
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
     }
 };
+
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 MFMA (v_mfma_f32_32x32x2_f32), 64 x 64 tiles
 // ---------------------------------------------------------------------------

@@ -9,9 +9,11 @@
 
 namespace fa {
 
-// Query rows per workgroup of the 16-bit kernels (4 waves x 32 rows); the
-// host sizes the grid with it.
-constexpr int kTileQ16 = 128;
+// Query rows per workgroup of the 16-bit kernels (the same for every
+// element type and head dimension); the host sizes the grid with it.
+constexpr int tile_q16(bool causal) {
+    return causal ? Fwd16<BF16, 128, true, false, false>::BQ : Fwd16<BF16, 128, false, false, false>::BQ;
+}
 
 #define FA_DECLARE16(T, D, C) \
     int launch16_##T##_d##D##_c##C(const FwdParams& p, int out_f32, bool count, void* stream);
