@@ -43,10 +43,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_n4096_counters.t
 
 
 def kernel_hash():
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that only a change of code invalidates the stored counter readings."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -177,12 +183,23 @@ def summarize(kind, paths):
             return list(csv.DictReader(f))
 
     if kind == "trace":
+        # the last `last` dispatches of a kernel are the launches the bench
+        # times one by one (its launch_ms)
+        last = int(paths[1]) if len(paths) > 1 else 100
+        durs = {}
+        for r in sorted(rows(paths[0], "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"| kernel | calls | average us | min us | max us | average of the last {last} us |")
+        print("|---|---|---|---|---|---|")
         for r in rows(paths[0], "*kernel_stats.csv"):
             name = r["Name"]
             if "fa::" not in name:
                 continue
+            tail = durs.get(name, [])[-last:]
+            tail_avg = f"{sum(tail) / len(tail):.1f}" if tail else "-"
             print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {tail_avg} |")
         return
     per = {}
     for d in paths:
@@ -242,7 +259,7 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
-                         "'trace DIR' or 'counters FETCH_DIR WRITE_DIR'")
+                         "'trace DIR [STEPS]' or 'counters FETCH_DIR WRITE_DIR'")
     a = ap.parse_args()
     if a.summarize:
         summarize(a.summarize[0], a.summarize[1:])

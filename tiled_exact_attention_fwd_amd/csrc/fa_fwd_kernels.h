@@ -11,8 +11,9 @@
 // log-sum-exp per row).
 //
 // MI355X mapping (16-bit inputs):
-//   * One workgroup = 4 waves = one 128-row query tile of one (batch, head).
-//     Each wave owns 32 query rows for the whole key loop.
+//   * One workgroup = one query tile of one (batch, head): 8 waves / 256 rows
+//     without a mask, 4 waves / 128 rows causal.  Each wave owns 32 query rows
+//     for the whole key loop.
 //   * The scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 32 key scores of ONE
 //     query, so the row sums are in-lane reductions plus one permlane32
@@ -151,8 +152,9 @@ struct FwdParams {
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16)
 //
-// One workgroup = 4 waves = a 128-row query tile of one (batch, head); each
-// wave owns 32 query rows for the whole key loop; two workgroups share a CU.
+// One workgroup = a query tile of one (batch, head), 32 query rows per wave
+// for the whole key loop (8 waves without a mask, 4 causal: two waves per
+// SIMD either way).
 // Key tiles are 64 rows.
 //
 // Per key tile t a wave does three things: the scores S_t = K_t Q^T (16 MFMA
