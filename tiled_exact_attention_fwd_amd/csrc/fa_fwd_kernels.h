@@ -245,6 +245,9 @@ struct Fwd16 {
     static constexpr int NV = BK / 2;              // scores per lane per tile
     static constexpr int LOADS = TILEB / (NT * 16);// 16-byte copies per thread per tile
     static constexpr int PD = 3;                   // operand prefetch distance (slots)
+    // issue a slot's LDS operand read before its softmax stages (measured
+    // ~1% faster with four waves, ~1% slower with eight)
+    static constexpr bool READ_FIRST = WAVES == 4;
     static constexpr int LDS = 4 * TILEB;
     static_assert(D == 64 || D == 128, "head dimension");
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile copy");
@@ -576,13 +579,18 @@ struct Fwd16 {
                     else copy_part(rvt, vfill, wave, voff_c[cu - LOADS], cu - LOADS);
                 }
                 slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pk, qreg);
+                if constexpr (READ_FIRST && i + PD < NSLOT) {
+                    opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 static_for<0, NPAIR>([&](auto K) {
                     constexpr int k = decltype(K)::value;
                     if constexpr (pair_slot(k) == i) stage_a(scur, k, st, c, xs[k][0], xs[k][1]);
                     if constexpr (pair_slot(k) + DB_ == i) stage_b(xs[k][0], xs[k][1]);
                     if constexpr (pair_slot(k) + DC_ == i) stage_c(pk, k, st, xs[k][0], xs[k][1]);
                 });
-                if constexpr (i + PD < NSLOT) opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
+                if constexpr (!READ_FIRST && i + PD < NSLOT)
+                    opnd[(i + PD) % (PD + 1)] = slot_operand(i + PD, kread, vread, ln);
                 __builtin_amdgcn_sched_barrier(0);
             });
 
