@@ -412,6 +412,8 @@ struct Fwd16 {
     }
 
     static __device__ void run(const FwdParams& p) {
+        // K and V double buffers (separate arrays: the compiler then knows
+        // that the buffers being read never alias the ones being filled)
         __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILEB];
         __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILEB];
         __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILEB];
@@ -636,26 +638,55 @@ struct Fwd16 {
             }
         }
 
-        // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S)) = (mc + log2 l) ln 2
+        // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S)) = (mc + log2 l) ln 2.
+        // Lane (li, lh) holds d = 32 db + 8 jj + 4 lh + (0..3) of row q0w + li.
         const float l = st.l;
-        if (qrow < N) {
-            const float inv = 1.0f / l;
-            const size_t orow = head_elems + (size_t)qrow * D;
+        const float inv = 1.0f / l;
+        if (OUT_F32) {
+            if (qrow < N) {
+                const size_t orow = head_elems + (size_t)qrow * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int d0 = 32 * db + 8 * jj + 4 * lh;
+                        *(f32x4_t*)((float*)p.o + orow + d0) =
+                            f32x4_t{acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv,
+                                    acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv};
+                    }
+            }
+        } else {
+            // The 16-bit output leaves through LDS so that every store writes
+            // whole rows (stored straight from the registers, each store
+            // would scatter 8-byte pieces over 32 rows).  The barrier frees
+            // the K / V buffers: every wave has passed its last read and its
+            // copies have landed.  Each wave stages its 32 rows in its own
+            // half of one buffer, 16-byte chunks XOR-swizzled by row against
+            // bank conflicts, then stores 16 bytes per lane, CPR lanes per row.
+            constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+            constexpr int RPS = 64 / CPR;               // rows per store
+            static_assert(2 * 32 * ROWB <= TILEB && WAVES <= 8, "output staging");
+            __syncthreads();
+            const int sb = wave >> 1;
+            uint8_t* const ost = (sb == 0 ? kbuf0 : sb == 1 ? kbuf1 : sb == 2 ? vbuf0 : vbuf1) + (wave & 1) * 32 * ROWB;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int d0 = 32 * db + 8 * jj + 4 * lh;
+                    const int c = 4 * db + jj;          // chunk of d = 32 db + 8 jj .. +7
                     const float o0 = acc[db][4 * jj + 0] * inv, o1 = acc[db][4 * jj + 1] * inv;
                     const float o2 = acc[db][4 * jj + 2] * inv, o3 = acc[db][4 * jj + 3] * inv;
-                    if (OUT_F32) {
-                        *(f32x4_t*)((float*)p.o + orow + d0) = f32x4_t{o0, o1, o2, o3};
-                    } else {
-                        *(u32x2_t*)((uint16_t*)p.o + orow + d0) = u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)};
-                    }
+                    *(u32x2_t*)(ost + li * ROWB + ((c ^ (li % CPR)) << 4) + 8 * lh) =
+                        u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)};
                 }
-            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
+#pragma unroll
+            for (int i = 0; i < 32 / RPS; ++i) {
+                const int r = i * RPS + lane / CPR, c = lane % CPR;
+                const u32x4_t v = *(const u32x4_t*)(ost + r * ROWB + ((c ^ (r % CPR)) << 4));
+                if (q0w + r < N) *(u32x4_t*)((uint16_t*)p.o + head_elems + (size_t)(q0w + r) * D + 8 * c) = v;
+            }
         }
+        if (lh == 0 && qrow < N) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
     }
 };
