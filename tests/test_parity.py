@@ -207,6 +207,15 @@ def test_deterministic_and_entry_points_agree():
         o2, l2 = fa.attention(qd, kd, vd, causal=True, scale=s)
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # d = 128 under both masks (the two workgroup shapes), ragged N
+    words = W.make_words((2, 8, 1500, 128), "bf16", "normal", seed=5)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    for causal in (False, True):
+        o1, l1 = fa.attention(qd, kd, vd, causal=causal, scale=W.scale_for(128))
+        for _ in range(3):
+            o2, l2 = fa.attention(qd, kd, vd, causal=causal, scale=W.scale_for(128))
+            torch.cuda.synchronize()
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2), causal
     stream = torch.cuda.current_stream().cuda_stream
     for dtype, fn in (("bf16", fa.fa_fwd_bf16), ("f16", fa.fa_fwd_f16), ("f32", fa.fa_fwd_f32)):
         w = W.make_words((1, 2, 130, 128), dtype, "normal", seed=4)

@@ -447,6 +447,11 @@ struct Fwd16 {
         int wend = q0w < N ? (CAUSAL ? min(jend, (q0w + 31) / BK + 1) : jend) : 0;
         wend = __builtin_amdgcn_readfirstlane(wend);
 
+        // (All of a wave's own LDS writes -- this zero fill, the output
+        // staging -- happen while none of its direct-to-LDS copies is in
+        // flight: the fill comes before the first copy, the staging after a
+        // barrier that waits for every copy.  A fill issued behind the first
+        // copy gave nondeterministic results.)
         // Both V buffers start as zeros: the first two iterations multiply
         // them with zero terms, and rows past N of a ragged last tile stay
         // zero whether or not the copy unit writes out-of-range rows.  The K
