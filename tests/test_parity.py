@@ -234,6 +234,30 @@ def test_deterministic_and_entry_points_agree():
         assert torch.equal(o, ref_o)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(5, 8, 4100, 64), (4, 16, 4096, 128), (1, 5, 700, 128)])
+def test_causal_tile_order_covers_every_tile(B, H, N, d):
+    """Causal launches issue query tiles longest first, in groups of heads
+    per XCD: with 256 CUs, 40 heads of 33 query tiles form groups of 4 and 1
+    head per XCD, 64 heads (the C3 shape) two groups of 4, and 5 heads (not
+    a multiple of 8) take the order across all heads.  Every (head, query
+    tile) is computed exactly once: the bits equal one launch per head, and
+    the tile counts equal the oracle's."""
+    words = W.make_words((B, H, N, d), "bf16", "normal", seed=11)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    s = W.scale_for(d)
+    o, lse = fa.attention(qd, kd, vd, causal=True, scale=s)
+    _, _, cnt = fa.attention(qd, kd, vd, causal=True, scale=s, counters=True)
+    torch.cuda.synchronize()
+    assert cnt == expected_counts("bf16", d, N, True, B * H)
+    for b in range(B):
+        for h in range(H):
+            q1, k1, v1 = (t[b:b + 1, h:h + 1].contiguous() for t in (qd, kd, vd))
+            o1, l1 = fa.attention(q1, k1, v1, causal=True, scale=s)
+            torch.cuda.synchronize()
+            assert torch.equal(o[b, h].view(torch.int16), o1[0, 0].view(torch.int16)), (b, h)
+            assert torch.equal(lse[b, h], l1[0, 0]), (b, h)
+
+
 def test_guard_bands_untouched():
     """Ragged N: nothing is written outside o and lse."""
     B, H, N, d = 3, 5, 1000, 64

@@ -25,6 +25,7 @@ using fa::FwdParams;
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];     // compute units, once known
 
 int elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
@@ -70,24 +71,27 @@ int check_args(const fa_fwd_args* a) {
     return FA_OK;
 }
 
-int check_device() {
+int check_device(int* cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
-    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
     if (st == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
         st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        g_dev_state[dev].store(st, std::memory_order_relaxed);
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_dev_state[dev].store(st, std::memory_order_release);
     }
+    *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
     return st == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
 }
 
 int run(const fa_fwd_args* a) {
     int st = check_args(a);
     if (st != FA_OK) return st;
-    st = check_device();
+    int cus = 0;
+    st = check_device(&cus);
     if (st != FA_OK) return st;
 
     int tq, tk;
@@ -100,7 +104,10 @@ int run(const fa_fwd_args* a) {
     p.lse = a->lse;
     p.N = a->N;
     p.tiles_q = (a->N + tq - 1) / tq;
-    p.total = a->B * a->H * p.tiles_q;
+    p.heads = a->B * a->H;
+    p.total = p.heads * p.tiles_q;
+    const int resident = a->dtype == FA_DTYPE_F32 ? fa::resident32() : fa::resident16(a->causal != 0);
+    p.group = fa::causal_group(p.heads, p.tiles_q, cus / fa::kNumXcd * resident);
     // softmax in base 2: exp(scale * s) = 2^(s * |scale| * log2 e) after a sign
     // flip of Q for negative scales; FLT_MIN keeps -inf * c at -inf for scale 0
     p.c = std::fmax(std::fabs(a->scale) * 1.4426950408889634f, FLT_MIN);

@@ -35,8 +35,8 @@
 //   * exp is v_exp_f32 (2^x) with log2(e) folded into the scale.
 //   * Workgroups are renumbered so that the query tiles of one head run on
 //     one XCD (dispatch is round-robin over the 8 XCDs): the head's K and V
-//     are then re-read from that XCD's L2.  Causal launches issue the
-//     longest query tiles first.
+//     are then re-read from that XCD's L2.  Causal launches issue query
+//     tiles longest first across all heads, which balances the CUs' loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -142,12 +142,65 @@ struct FwdParams {
     void* o;
     float* lse;
     int N;
+    int heads;          // B * H
     int tiles_q;        // ceil(N / BQ)
-    int total;          // B * H * tiles_q
+    int total;          // heads * tiles_q
+    int group;          // heads per group of the causal tile order
     float c;            // |scale| * log2(e), at least FLT_MIN
     uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
     unsigned long long* counters;
 };
+
+// Workgroup index -> (head, query tile).
+//
+// Without a mask every query tile costs the same; each XCD receives a
+// contiguous range of logical tiles (head-major), so that a head's K and V
+// are re-read from one L2.
+//
+// Under the causal mask query tile i costs i + 1 key-tile steps.  The
+// dispatcher starts workgroups in index order as slots free up, so tiles are
+// issued longest first (by rank = tiles_q - 1 - i), which ends the launch
+// with the short ones.  With a head count divisible by 8, XCD x (which runs
+// workgroups b = x mod 8) owns heads x, x + 8, ... and takes them in groups
+// of `group` heads, rank-major inside a group: a group's tiles fill the
+// XCD's workgroup slots, and only its few heads' K and V are live in the L2
+// at a time.  Otherwise tiles go rank-major across all heads.
+struct TileId {
+    int hh, qi;
+};
+template <bool CAUSAL>
+__device__ __forceinline__ TileId tile_of(int bid, const FwdParams& p) {
+    if (!CAUSAL) {
+        const int L = xcd_remap(bid, p.total);
+        const int hh = L / p.tiles_q;
+        return {hh, L - hh * p.tiles_q};
+    }
+    if (p.heads % kNumXcd == 0) {
+        const int x = bid % kNumXcd, s = bid / kNumXcd;   // s < heads / 8 * tiles_q
+        const int hpx = p.heads / kNumXcd;
+        const int gsz = p.group * p.tiles_q;
+        const int g = s / gsz, w = s - g * gsz;
+        const int gg = min(p.group, hpx - g * p.group);   // heads in this group
+        const int rank = w / gg;
+        return {(g * p.group + w - rank * gg) * kNumXcd + x, p.tiles_q - 1 - rank};
+    }
+    const int rank = bid / p.heads;
+    return {bid - rank * p.heads, p.tiles_q - 1 - rank};
+}
+
+// Heads per group of the causal order above: enough for the group's query
+// tiles to fill the workgroup slots of one XCD twice, at most the XCD's
+// heads.  (Measured on the 4096-row, 64-head causal launch: groups of 2
+// heads, which fill the slots once, leave the last group's long tiles
+// running alone at the end; 4 heads balance as well as all 8.  On the
+// 1000-row, 512-head launch groups of 16 heads beat 8 and 64: larger groups
+// spread each head's K and V reuse out of the L2.)
+inline int causal_group(int heads, int tiles_q, int slots_per_xcd) {
+    if (heads % kNumXcd != 0) return 1;
+    const int g = (2 * slots_per_xcd + tiles_q - 1) / tiles_q;
+    const int hpx = heads / kNumXcd;
+    return g < 1 ? 1 : (g > hpx ? hpx : g);
+}
 
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16)
@@ -207,6 +260,11 @@ __device__ __forceinline__ u32x2_t lds_read_tr(const uint8_t* p) {
 // keeps a value's computation at this point of the instruction stream: the
 // compiler may not sink it past here (the MFMA interleave depends on it)
 template <class X> __device__ __forceinline__ void pin(X& x) { asm volatile("" : "+v"(x)); }
+// the value of a wave-uniform x, held in SGPRs from this point on
+template <class X> __device__ __forceinline__ X pin_s(X x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <int I> struct IntTag { static constexpr int value = I; };
@@ -227,10 +285,12 @@ struct Fwd16 {
     // tile copy without a mask: half the L2 -> LDS traffic of four.  Causal
     // launches keep four waves (128 rows, two workgroups per CU): their
     // waves' work differs along the diagonal, and a smaller workgroup waits
-    // less at its barriers for the wave with the most keys.
+    // less at its barriers for the wave with the most keys (under the
+    // longest-first tile order eight waves measure the same).
     static constexpr int WAVES = CAUSAL ? 4 : 8;
     static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
     static constexpr int OCC = 2;                  // waves per SIMD
+    static constexpr int RESIDENT = 4 * OCC / WAVES;   // workgroups per CU
     static constexpr int NT = 64 * WAVES;
     static constexpr int BK = 64;                  // keys per tile
     static constexpr int ROWB = 2 * D;             // bytes per K / V row
@@ -423,12 +483,18 @@ struct Fwd16 {
         const int lane = tid & 63;
         const int li = lane & 31, lh = lane >> 5;
         const int N = p.N;
+        // Every kernel argument is read into SGPRs here, before the first
+        // direct-to-LDS copy: a scalar load issued while a copy is in flight
+        // could target SGPRs that the copy still reads (its buffer resource
+        // or M0 source).
+        void* const out = pin_s(p.o);
+        float* const lse = pin_s(p.lse);
+        unsigned long long* const counters = pin_s(p.counters);
+        const float c = pin_s(p.c);
 
-        const int L = xcd_remap(blockIdx.x, p.total);
-        const int hh = L / p.tiles_q;
-        int qi = L - hh * p.tiles_q;
-        if (CAUSAL) qi = p.tiles_q - 1 - qi;
-        const int qt0 = qi * BQ;
+        const TileId t = tile_of<CAUSAL>(blockIdx.x, p);
+        const int hh = t.hh;
+        const int qt0 = t.qi * BQ;
         const int q0w = qt0 + wave * 32;            // first row of this wave; lane li holds row q0w + li
         const int qrow = q0w + li;
 
@@ -503,7 +569,6 @@ struct Fwd16 {
         // it through the slow path that sets the real one
         st.mc = -__FLT_MAX__;
         st.l = st.lt = 0.f;
-        const float c = p.c;
 
         // this thread's byte offsets inside a K / V tile, one per copy
         const uint32_t ksrc = copy_offset<true>(wave, lane);
@@ -655,7 +720,7 @@ struct Fwd16 {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int d0 = 32 * db + 8 * jj + 4 * lh;
-                        *(f32x4_t*)((float*)p.o + orow + d0) =
+                        *(f32x4_t*)((float*)out + orow + d0) =
                             f32x4_t{acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv,
                                     acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv};
                     }
@@ -688,11 +753,11 @@ struct Fwd16 {
             for (int i = 0; i < 32 / RPS; ++i) {
                 const int r = i * RPS + lane / CPR, c = lane % CPR;
                 const u32x4_t v = *(const u32x4_t*)(ost + r * ROWB + ((c ^ (r % CPR)) << 4));
-                if (q0w + r < N) *(u32x4_t*)((uint16_t*)p.o + head_elems + (size_t)(q0w + r) * D + 8 * c) = v;
+                if (q0w + r < N) *(u32x4_t*)((uint16_t*)out + head_elems + (size_t)(q0w + r) * D + 8 * c) = v;
             }
         }
-        if (lh == 0 && qrow < N) p.lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
-        if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
+        if (lh == 0 && qrow < N) lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
+        if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(counters, qt0, jend, N);
     }
 };
 
@@ -705,6 +770,7 @@ struct Fwd32 {
     static constexpr int BQ = 64;                  // 2 waves x 32 query rows
     static constexpr int WAVES = 2;
     static constexpr int OCC = 1;
+    static constexpr int RESIDENT = 4 * OCC / WAVES;   // workgroups per CU
     static constexpr int NT = 64 * WAVES;
     static constexpr int BK = 64;
     static constexpr int NMB = BK / 32;
@@ -726,11 +792,9 @@ struct Fwd32 {
         const int li = lane & 31, lh = lane >> 5;
         const int N = p.N;
 
-        const int L = xcd_remap(blockIdx.x, p.total);
-        const int hh = L / p.tiles_q;
-        int qi = L - hh * p.tiles_q;
-        if (CAUSAL) qi = p.tiles_q - 1 - qi;
-        const int qt0 = qi * BQ;
+        const TileId t = tile_of<CAUSAL>(blockIdx.x, p);
+        const int hh = t.hh;
+        const int qt0 = t.qi * BQ;
         const int q0w = qt0 + wave * 32;
         const int qrow = q0w + li;
 

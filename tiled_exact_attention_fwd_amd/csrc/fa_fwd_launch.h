@@ -14,6 +14,12 @@ namespace fa {
 constexpr int tile_q16(bool causal) {
     return causal ? Fwd16<BF16, 128, true, false, false>::BQ : Fwd16<BF16, 128, false, false, false>::BQ;
 }
+// Workgroups of one kernel resident on a CU at a time (the causal tile
+// order groups heads by it)
+constexpr int resident16(bool causal) {
+    return causal ? Fwd16<BF16, 128, true, false, false>::RESIDENT : Fwd16<BF16, 128, false, false, false>::RESIDENT;
+}
+constexpr int resident32() { return Fwd32<64, true, false>::RESIDENT; }
 
 #define FA_DECLARE16(T, D, C) \
     int launch16_##T##_d##D##_c##C(const FwdParams& p, int out_f32, bool count, void* stream);
