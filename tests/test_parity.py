@@ -258,6 +258,26 @@ def test_causal_tile_order_covers_every_tile(B, H, N, d):
             assert torch.equal(lse[b, h], l1[0, 0]), (b, h)
 
 
+@pytest.mark.parametrize("dtype,B,H,N,d,scale", [
+    ("bf16", 4, 80, 300, 64, None),     # 640 query tiles: 3 or 2 per workgroup; ragged rows and keys
+    ("f16", 2, 72, 520, 128, -0.3),     # 432 query tiles; last tile 8 rows; negative scale
+    ("bf16", 1, 300, 1000, 128, None),  # 1200 query tiles, 16 key tiles each
+])
+def test_persistent_kernel(dtype, B, H, N, d, scale):
+    """Plain launches without a mask and with more query tiles than the
+    device has workgroup slots run the persistent kernel, which pipelines
+    across query tiles; it matches the oracle on every head, gives the same
+    bits as the per-tile kernel (the counters launch in launch_all), and
+    repeats bit for bit."""
+    words = W.make_words((B, H, N, d), dtype, "normal", seed=21)
+    s = W.scale_for(d) if scale is None else scale
+    _, (qd, kd, vd, o, lse, _) = check_against_oracle(words, dtype, False, s, what="persistent")
+    for _ in range(2):
+        o2, l2 = fa.attention(qd, kd, vd, causal=False, scale=s)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+
+
 def test_guard_bands_untouched():
     """Ragged N: nothing is written outside o and lse."""
     B, H, N, d = 3, 5, 1000, 64

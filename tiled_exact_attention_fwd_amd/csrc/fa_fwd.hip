@@ -117,6 +117,18 @@ int run(const fa_fwd_args* a) {
     const bool count = a->counters != nullptr;
 
     const int c = a->causal, o32 = a->out_dtype;
+    // A plain 16-bit launch without a mask that has more query tiles than
+    // the device has workgroup slots runs the persistent kernel: one
+    // workgroup per slot (a multiple of 8, so that each keeps to one XCD's
+    // tiles) takes every slots-th query tile and pipelines across them.
+    const int slots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(false);
+    const int nk = (a->N + tk - 1) / tk;
+    if (!c && a->dtype != FA_DTYPE_F32 && !o32 && !count && slots > 0 && p.total > slots &&
+        nk >= fa::persistent_min_key_tiles()) {
+        if (a->dtype == FA_DTYPE_BF16)
+            return a->d == 64 ? fa::launch16p_bf16_d64(p, slots, a->stream) : fa::launch16p_bf16_d128(p, slots, a->stream);
+        return a->d == 64 ? fa::launch16p_f16_d64(p, slots, a->stream) : fa::launch16p_f16_d128(p, slots, a->stream);
+    }
     switch (a->dtype) {
     case FA_DTYPE_BF16:
         if (a->d == 64) return c ? fa::launch16_bf16_d64_c1(p, o32, count, a->stream)
@@ -190,7 +202,8 @@ const char* fa_strerror(int status) {
 
 const char* fa_build_info(void) {
     return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
-           "; kernels: bf16/f16 d64 and d128 (256x64 tiles non-causal, 128x64 causal, 32 query rows per wave), causal on/off, "
+           "; kernels: bf16/f16 d64 and d128 (256x64 tiles non-causal, 128x64 causal, 32 query rows per wave; "
+           "persistent across query tiles without a mask), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off";
 }
 

@@ -37,6 +37,10 @@
 //     one XCD (dispatch is round-robin over the 8 XCDs): the head's K and V
 //     are then re-read from that XCD's L2.  Causal launches issue query
 //     tiles longest first across all heads, which balances the CUs' loads.
+//   * Without a mask, launches with more query tiles than workgroup slots
+//     run a persistent variant (Fwd16P): one workgroup per CU runs the key
+//     loops of its query tiles back to back as one software pipeline, so the
+//     pipeline does not drain and refill between query tiles.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -265,6 +269,13 @@ template <class X> __device__ __forceinline__ X pin_s(X x) {
     asm volatile("" : "+s"(x));
     return x;
 }
+// A store to global memory.  Pointers that went through pin_s have lost
+// their address space; a generic (flat) store counts on the LDS counter as
+// well, and inside the key loop it would make every LDS operand wait a full
+// drain of that counter.
+template <class X> __device__ __forceinline__ void gstore(void* p, const X& v) {
+    *(__attribute__((address_space(1))) X*)p = v;
+}
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <int I> struct IntTag { static constexpr int value = I; };
@@ -443,9 +454,10 @@ struct Fwd16 {
     // larger of it and the tile's maximum; the running output and sum are
     // rescaled by the correction exp2(old - new) and the tile's terms and sum
     // are recomputed.  Other lanes keep their reference and terms (their
-    // correction is 1).
+    // correction is 1).  keep_acc leaves the accumulators alone (they hold
+    // another query tile's output when the persistent kernel starts a tile).
     static __device__ void raise_reference(const f32x16_t* scur, u32x4_t* pcur, Soft& st, float c,
-                                           f32x16_t* acc, bool need) {
+                                           f32x16_t* acc, bool need, bool keep_acc = false) {
         float mx = -__builtin_inff();
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
@@ -457,8 +469,9 @@ struct Fwd16 {
         st.mc = nmc;
         st.meff = nmc;
         st.l *= alpha;
+        const float aacc = keep_acc ? 1.0f : alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        for (int db = 0; db < NDB; ++db) acc[db] *= aacc;
         float lt = 0.f;
 #pragma unroll
         for (int k = 0; k < NPAIR; ++k) {
@@ -720,9 +733,9 @@ struct Fwd16 {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int d0 = 32 * db + 8 * jj + 4 * lh;
-                        *(f32x4_t*)((float*)out + orow + d0) =
-                            f32x4_t{acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv,
-                                    acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv};
+                        gstore((float*)out + orow + d0,
+                               f32x4_t{acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv,
+                                       acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv});
                     }
             }
         } else {
@@ -753,11 +766,354 @@ struct Fwd16 {
             for (int i = 0; i < 32 / RPS; ++i) {
                 const int r = i * RPS + lane / CPR, c = lane % CPR;
                 const u32x4_t v = *(const u32x4_t*)(ost + r * ROWB + ((c ^ (r % CPR)) << 4));
-                if (q0w + r < N) *(u32x4_t*)((uint16_t*)out + head_elems + (size_t)(q0w + r) * D + 8 * c) = v;
+                if (q0w + r < N) gstore((uint16_t*)out + head_elems + (size_t)(q0w + r) * D + 8 * c, v);
             }
         }
-        if (lh == 0 && qrow < N) lse[(size_t)hh * N + qrow] = (st.mc + __log2f(l)) * kLn2;
+        if (lh == 0 && qrow < N) gstore(lse + (size_t)hh * N + qrow, (st.mc + __log2f(l)) * kLn2);
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(counters, qt0, jend, N);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Persistent 16-bit kernel without a mask (16-bit output, no counters).
+//
+// One workgroup per CU stays resident and takes the query tiles b, b + G,
+// b + 2 G, ... of the logical order above (G workgroups; with G a multiple
+// of 8 every tile of a workgroup lies on its XCD's range).  Its waves run
+// the key loops of those tiles back to back as one stream of key tiles, so
+// the software pipeline of Fwd16 neither drains nor refills between query
+// tiles: while the output MFMAs finish a tile's last key tile, the score
+// MFMAs already run on the next tile's first.  At the iteration whose
+// softmax takes key tile j of a query tile (nk key tiles per query tile):
+//   j = 0       the previous query tile's LSE is stored and the softmax
+//               state restarts; the first-key slow path leaves the
+//               accumulators alone (they still hold that tile's output);
+//   j = 1       the previous tile's output, final after the output MFMAs of
+//               iteration j = 0, leaves through LDS (right after the barrier,
+//               before any copy of the iteration is issued), and the
+//               accumulators clear;
+//   j = 2       the next tile's Q rows are copied HBM -> LDS (direct-to-LDS
+//               loads into the wave's own staging slice);
+//   j = nk - 1  the next tile's Q^T operands are read from that slice: the
+//               score MFMAs of this iteration start the next tile.
+// The host uses it for nk >= 4, where these are four different iterations.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+struct Fwd16P {
+    using Bs = Fwd16<T, D, false, false, false>;
+    static constexpr int WAVES = Bs::WAVES, BQ = Bs::BQ, OCC = Bs::OCC, NT = Bs::NT, BK = Bs::BK;
+    static constexpr int RESIDENT = Bs::RESIDENT;
+    static constexpr int ROWB = Bs::ROWB, TILEB = Bs::TILEB, NS = Bs::NS, NDB = Bs::NDB, NMB = Bs::NMB;
+    static constexpr int NKS = Bs::NKS, NSLOT = Bs::NSLOT, NPAIR = Bs::NPAIR, PD = Bs::PD, LOADS = Bs::LOADS;
+    static constexpr int DB_ = Bs::DB_, DC_ = Bs::DC_, COPY_EVERY = Bs::COPY_EVERY, NCOPY = Bs::NCOPY;
+    static constexpr bool READ_FIRST = Bs::READ_FIRST;
+    static constexpr int SLICE = 32 * ROWB;          // one wave's Q / O staging bytes
+    static constexpr int QLOADS = SLICE / 1024;      // 16-byte copies per lane of a wave's Q rows
+    static constexpr int MIN_KEY_TILES = 4;
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPS = 64 / CPR;             // rows per 16-byte store
+    static_assert(RESIDENT == 1 && SLICE % 1024 == 0, "persistent shape");
+
+    // The lane index, opaque to the optimiser: addresses derived from it in a
+    // once-per-tile block are computed there, not hoisted out of the key loop
+    // into registers that would stay live through it.
+    static __device__ __forceinline__ int opaque_lane(int lane) {
+        asm volatile("" : "+v"(lane));
+        return lane;
+    }
+
+    struct TileInfo {
+        size_t hoff;        // byte offset of the head in Q, K, V and O
+        int hh;             // head (batch * H + h)
+        int qt0;            // first query row
+    };
+
+    // Output of one query tile: acc / l rounded to 16 bits, staged in the
+    // wave's slice (16-byte chunks XOR-swizzled by row), stored as whole rows.
+    // Inside the key loop every other register is live, so the pieces go one
+    // at a time (scheduling barriers keep the compiler from computing them
+    // all first).
+    static __device__ __forceinline__ void store_output(const f32x16_t* acc, float inv, uint8_t* ost, void* out,
+                                                        const TileInfo& t, int wave, int lane, int N) {
+        lane = opaque_lane(lane);
+        const int li = lane & 31, lh = lane >> 5;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int c = 4 * db + jj;
+                const float o0 = acc[db][4 * jj + 0] * inv, o1 = acc[db][4 * jj + 1] * inv;
+                const float o2 = acc[db][4 * jj + 2] * inv, o3 = acc[db][4 * jj + 3] * inv;
+                *(u32x2_t*)(ost + li * ROWB + ((c ^ (li % CPR)) << 4) + 8 * lh) =
+                    u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)};
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        const int q0w = t.qt0 + wave * 32;
+        uint8_t* const obase = (uint8_t*)out + t.hoff;
+#pragma unroll
+        for (int i = 0; i < 32 / RPS; ++i) {
+            const int r = i * RPS + lane / CPR, c = lane % CPR;
+            const u32x4_t v = *(const u32x4_t*)(ost + r * ROWB + ((c ^ (r % CPR)) << 4));
+            if (q0w + r < N) gstore(obase + (size_t)(q0w + r) * ROWB + 16 * c, v);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    static __device__ void run(const FwdParams& p) {
+        __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILEB];
+        __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TILEB];
+        // (less aligned than the K / V buffers, which the allocator then
+        // places first: their operand reads keep addresses below 64 KiB,
+        // which the 16-bit offset field of an LDS instruction can reach)
+        __shared__ __attribute__((aligned(256))) uint8_t qbuf[WAVES * SLICE];
+        const int tid = threadIdx.x;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        const int li = lane & 31, lh = lane >> 5;
+        const int N = p.N;
+        // every kernel argument in SGPRs before the first direct-to-LDS copy
+        void* const out = pin_s(p.o);
+        float* const lse = pin_s(p.lse);
+        const float c = pin_s(p.c);
+        const uint32_t qsign = pin_s(p.qsign);
+        const uint8_t* const qptr = (const uint8_t*)pin_s(p.q);
+        const uint8_t* const kptr = (const uint8_t*)pin_s(p.k);
+        const uint8_t* const vptr = (const uint8_t*)pin_s(p.v);
+        const int tiles_q = pin_s(p.tiles_q);
+        const int total = pin_s(p.total);
+
+        const int G = gridDim.x, b = blockIdx.x;
+        const int ntiles = (total - b + G - 1) / G;     // b < total
+        const int nk = (N + BK - 1) / BK;               // >= MIN_KEY_TILES
+        int gend = ntiles * nk;                         // key tiles of this workgroup
+        asm volatile("" : "+s"(gend));
+        const uint32_t head_bytes = (uint32_t)N * ROWB;
+        uint8_t* const qslice = qbuf + wave * SLICE;
+
+        auto decode = [&](int k) {
+            const int L = xcd_remap(b + min(k, ntiles - 1) * G, total);
+            const int hh = L / tiles_q;
+            return TileInfo{(size_t)hh * head_bytes, hh, (L - hh * tiles_q) * BQ};
+        };
+        TileInfo cur = decode(0), nxt = decode(1), prv = cur;
+
+        // zero fill before the first copy (see Fwd16)
+#pragma unroll
+        for (int i = tid; i < TILEB / 16; i += NT) {
+            ((u32x4_t*)vbuf0)[i] = u32x4_t{0, 0, 0, 0};
+            ((u32x4_t*)vbuf1)[i] = u32x4_t{0, 0, 0, 0};
+            ((u32x4_t*)kbuf1)[i] = u32x4_t{0, 0, 0, 0};
+        }
+
+        // Q^T operand of the first tile straight from HBM
+        u32x4_t qreg[NS];
+        {
+            const auto rq = make_rsrc(qptr + cur.hoff, head_bytes);
+            const int qrow = cur.qt0 + wave * 32 + li;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                qreg[s] = buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * lh) * 2);
+                qreg[s] ^= qsign;
+            }
+        }
+
+        typename Bs::Lane ln;
+        {
+            const int prow = Bs::perm_row(li);
+            const int ks_sw = Bs::fk(prow);
+#pragma unroll
+            for (int ks = 0; ks < NS; ++ks) ln.koff[ks] = prow * ROWB + (((2 * ks + lh) ^ ks_sw) << 4);
+            const int Gq = lane >> 4, sq = lane & 15;
+            const int fvq = D == 128 ? ((sq >> 2) & 3) : ((sq >> 3) & 1);
+            const int y = 2 * (Gq & 1) + ((sq & 3) >> 1);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                ln.voff[db] = (8 * lh + (sq >> 2)) * ROWB + ((4 * (db ^ fvq) + y) << 4) + 8 * (sq & 1);
+        }
+
+        f32x16_t acc[NDB];
+        f32x16_t s0[NMB], s1[NMB];
+        u32x4_t pk[NKS];
+        typename Bs::Soft st;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) s0[mb] = s1[mb] = f32x16_t{};
+#pragma unroll
+        for (int kt = 0; kt < NKS; ++kt) pk[kt] = u32x4_t{0, 0, 0, 0};
+        st.mc = -__FLT_MAX__;
+        st.l = st.lt = 0.f;
+        float inv_prev = 0.f;
+
+        const uint32_t ksrc = Bs::template copy_offset<true>(wave, lane);
+        const uint32_t vsrc = Bs::template copy_offset<false>(wave, lane);
+        uint32_t koff_c[LOADS], voff_c[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            koff_c[u] = ksrc + (uint32_t)(u * WAVES * 1024);
+            voff_c[u] = vsrc + (uint32_t)(u * WAVES * 1024);
+        }
+
+        {   // K_0 of the first tile into kbuf0
+            const auto rk0 = make_rsrc(kptr + cur.hoff, head_bytes);
+#pragma unroll
+            for (int u = 0; u < LOADS; ++u) Bs::copy_part(rk0, kbuf0, wave, koff_c[u], u);
+        }
+
+        // position of the softmax stream: key tile j0 of this workgroup's
+        // query tile k0 (j0 = -1 before the first; j0 = nk until the wrap)
+        int k0 = 0, j0 = -1;
+        // iterations with 3 <= j0 <= nk - 3 are plain: one range check, the
+        // copy sources advance by a tile; every other one recomputes its
+        // state in one block
+        const uint32_t nk_s = nk > 5 ? (uint32_t)(nk - 5) : 0u;
+        const uint8_t* kc_ptr = kptr;      // K copy of this iteration (key tile g + 2)
+        const uint8_t* vc_ptr = vptr;      // V copy (key tile g)
+        uint32_t kc_ext = 0, vc_ext = 0;
+        bool sm_on = false;                // this wave has rows in the softmax tile
+
+        auto iteration = [&](const int g, auto odd_tag) {
+            constexpr bool ODD = decltype(odd_tag)::value;
+            uint8_t* kread = ODD ? kbuf0 : kbuf1;
+            uint8_t* kfill = ODD ? kbuf1 : kbuf0;
+            uint8_t* vread = ODD ? vbuf0 : vbuf1;
+            uint8_t* vfill = ODD ? vbuf1 : vbuf0;
+            f32x16_t* scur = ODD ? s1 : s0;
+            f32x16_t* snext = ODD ? s0 : s1;
+
+            __syncthreads();   // this wave's copies done (vmcnt 0), and everyone's
+
+            if ((uint32_t)(j0 - 3) >= nk_s) {
+                if (j0 == nk) {
+                    j0 = 0;
+                    ++k0;
+                }
+                if (j0 == 1 && k0 >= 1) {
+                    // the previous tile's output (no copy of this wave in flight)
+                    store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+                }
+                if (j0 == 0 && k0 >= 1) {
+                    // the tile k0 - 1 is complete: its LSE, and a fresh softmax state
+                    const int row = cur.qt0 + wave * 32 + li;
+                    if (lh == 0 && row < N) gstore(lse + (size_t)cur.hh * N + row, (st.mc + __log2f(st.l)) * kLn2);
+                    inv_prev = 1.0f / st.l;
+                    st.mc = -__FLT_MAX__;
+                    st.l = 0.f;
+                    prv = cur;
+                    cur = nxt;
+                    nxt = decode(k0 + 1);
+                }
+                if (j0 == 2 && k0 + 1 < ntiles) {
+                    // the next tile's Q rows into this wave's slice, chunks
+                    // XOR-swizzled by row as the operand reads below expect
+                    const uint32_t r0 = (uint32_t)(nxt.qt0 + wave * 32) * ROWB;
+                    const uint32_t ext = __builtin_amdgcn_readfirstlane(r0 < head_bytes ? head_bytes - r0 : 0u);
+                    const auto rq = make_rsrc(qptr + nxt.hoff + r0, ext);
+                    const int ol = opaque_lane(lane);
+#pragma unroll
+                    for (int u = 0; u < QLOADS; ++u) {
+                        const int o = u * 1024 + ol * 16, r = o / ROWB;
+                        const uint32_t src = (uint32_t)(r * ROWB + ((((o % ROWB) >> 4) ^ Bs::fk(r)) << 4));
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rq, (__attribute__((address_space(3))) void*)(qslice + u * 1024), 16, src, 0, 0, 0);
+                    }
+                }
+                if (j0 == nk - 1 && k0 + 1 < ntiles) {
+                    // the score MFMAs of this iteration start the next tile
+                    const int ol = opaque_lane(lane), oli = ol & 31, olh = ol >> 5;
+                    const uint8_t* qs = qslice + oli * ROWB;
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        qreg[s] = *(const u32x4_t*)(qs + (((2 * s + olh) ^ Bs::fk(oli)) << 4));
+                        qreg[s] ^= qsign;
+                    }
+                }
+                sm_on = j0 >= 0 && k0 < ntiles && cur.qt0 + wave * 32 < N;
+                const int kk0 = j0 * BK;
+                if (sm_on && kk0 + BK > N) {
+                    // the ragged last key tile
+                    const int lim = N - 1 - kk0 - 8 * lh;
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kk = 32 * mb + 16 * (r >> 3) + (r & 7);
+                            scur[mb][r] = kk > lim ? -__builtin_inff() : scur[mb][r];
+                        }
+                }
+                // copy sources: K of key tile g + 2 and V of key tile g of the
+                // stream (empty extents outside it)
+                const bool kin = j0 + 2 < nk;
+                const uint32_t kcopy = g + 2 < gend ? (uint32_t)((kin ? j0 + 2 : j0 + 2 - nk) * TILEB) : head_bytes;
+                const uint32_t vcopy = j0 >= 0 && g < gend ? (uint32_t)(j0 * TILEB) : head_bytes;
+                kc_ptr = kptr + (kin ? cur.hoff : nxt.hoff) + kcopy;
+                kc_ext = head_bytes - kcopy;
+                vc_ptr = vptr + cur.hoff + vcopy;
+                vc_ext = head_bytes - vcopy;
+            }
+            st.meff = sm_on ? st.mc : __builtin_inff();
+            st.lt = 0.f;
+            const auto rkt = make_rsrc(kc_ptr, kc_ext);
+            const auto rvt = make_rsrc(vc_ptr, vc_ext);
+
+            float xs[NPAIR][2];
+            u32x4_t opnd[PD + 1];
+            static_for<0, PD>([&](auto I) { opnd[I.value] = Bs::slot_operand(I.value, kread, vread, ln); });
+            static_for<0, NSLOT>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i % COPY_EVERY == 1 % COPY_EVERY && i / COPY_EVERY < NCOPY) {
+                    constexpr int cu = i / COPY_EVERY;
+                    if constexpr (cu < LOADS) Bs::copy_part(rkt, kfill, wave, koff_c[cu], cu);
+                    else Bs::copy_part(rvt, vfill, wave, voff_c[cu - LOADS], cu - LOADS);
+                }
+                Bs::slot_mfma(i, opnd[i % (PD + 1)], acc, snext, pk, qreg);
+                if constexpr (READ_FIRST && i + PD < NSLOT) {
+                    opnd[(i + PD) % (PD + 1)] = Bs::slot_operand(i + PD, kread, vread, ln);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                static_for<0, NPAIR>([&](auto K) {
+                    constexpr int k = decltype(K)::value;
+                    if constexpr (Bs::pair_slot(k) == i) Bs::stage_a(scur, k, st, c, xs[k][0], xs[k][1]);
+                    if constexpr (Bs::pair_slot(k) + DB_ == i) Bs::stage_b(xs[k][0], xs[k][1]);
+                    if constexpr (Bs::pair_slot(k) + DC_ == i) Bs::stage_c(pk, k, st, xs[k][0], xs[k][1]);
+                });
+                if constexpr (!READ_FIRST && i + PD < NSLOT)
+                    opnd[(i + PD) % (PD + 1)] = Bs::slot_operand(i + PD, kread, vread, ln);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+
+            float lt = sum_halves(st.lt);
+            const bool need = lt > Bs::kTileSumLimit || lt > st.l;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                Bs::raise_reference(scur, pk, st, c, acc, need, j0 == 0);
+                lt = sum_halves(st.lt);
+            }
+            st.l += lt;
+            // the next iteration's copy sources if it is a plain one (a
+            // recomputing one overwrites them; extents that hit zero here are
+            // only ever followed by recomputing iterations)
+            kc_ptr += TILEB;
+            kc_ext -= TILEB;
+            vc_ptr += TILEB;
+            vc_ext -= TILEB;
+            ++j0;
+        };
+
+        int gstart = -1;
+        asm volatile("" : "+s"(gstart));
+#pragma clang loop unroll(disable)
+        for (int g = gstart; g <= gend; g += 2) {
+            iteration(g, BoolTag<true>{});
+            if (g + 1 <= gend) iteration(g + 1, BoolTag<false>{});
+        }
+
+        // the last tile's output (its LSE was stored at the iteration g = gend)
+        __syncthreads();
+        store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
     }
 };
 

@@ -32,14 +32,22 @@ FA_DECLARE16(f16, 64, 1)
 FA_DECLARE16(f16, 128, 0)
 FA_DECLARE16(f16, 128, 1)
 #undef FA_DECLARE16
+// persistent kernels (no mask, 16-bit output, no counters; at least
+// persistent_min_key_tiles() key tiles), launched on `grid` workgroups
+int launch16p_bf16_d64(const FwdParams& p, int grid, void* stream);
+int launch16p_bf16_d128(const FwdParams& p, int grid, void* stream);
+int launch16p_f16_d64(const FwdParams& p, int grid, void* stream);
+int launch16p_f16_d128(const FwdParams& p, int grid, void* stream);
+constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TILES; }
 int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
 int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
 
 // launch of one kernel instance on the caller's stream
+// (one workgroup per query tile, or `grid` workgroups for a persistent kernel)
 template <class K>
-int launch_kernel(const FwdParams& p, void* stream) {
+int launch_kernel(const FwdParams& p, void* stream, int grid = 0) {
     void* args[] = {const_cast<FwdParams*>(&p)};
-    const hipError_t err = hipLaunchKernel((const void*)&fwd_kernel<K>, dim3(p.total), dim3(K::NT),
+    const hipError_t err = hipLaunchKernel((const void*)&fwd_kernel<K>, dim3(grid > 0 ? grid : p.total), dim3(K::NT),
                                           args, 0, (hipStream_t)stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
