@@ -262,6 +262,8 @@ def test_causal_tile_order_covers_every_tile(B, H, N, d):
     ("bf16", 4, 80, 300, 64, None),     # 640 query tiles: 3 or 2 per workgroup; ragged rows and keys
     ("f16", 2, 72, 520, 128, -0.3),     # 432 query tiles; last tile 8 rows; negative scale
     ("bf16", 1, 300, 1000, 128, None),  # 1200 query tiles, 16 key tiles each
+    ("bf16", 1, 300, 200, 128, None),   # 4 key tiles (every iteration a transition), 1 query tile per head
+    ("f16", 3, 100, 330, 64, 0.2),      # 6 key tiles (one plain iteration per tile), 2 query tiles per head
 ])
 def test_persistent_kernel(dtype, B, H, N, d, scale):
     """Plain launches without a mask and with more query tiles than the
