@@ -258,24 +258,28 @@ def test_causal_tile_order_covers_every_tile(B, H, N, d):
             assert torch.equal(lse[b, h], l1[0, 0]), (b, h)
 
 
-@pytest.mark.parametrize("dtype,B,H,N,d,scale", [
-    ("bf16", 4, 80, 300, 64, None),     # 640 query tiles: 3 or 2 per workgroup; ragged rows and keys
-    ("f16", 2, 72, 520, 128, -0.3),     # 432 query tiles; last tile 8 rows; negative scale
-    ("bf16", 1, 300, 1000, 128, None),  # 1200 query tiles, 16 key tiles each
-    ("bf16", 1, 300, 200, 128, None),   # 4 key tiles (every iteration a transition), 1 query tile per head
-    ("f16", 3, 100, 330, 64, 0.2),      # 6 key tiles (one plain iteration per tile), 2 query tiles per head
+@pytest.mark.parametrize("dtype,B,H,N,d,scale,causal", [
+    ("bf16", 4, 80, 300, 64, None, False),     # 640 query tiles: 3 or 2 per workgroup; ragged rows and keys
+    ("f16", 2, 72, 520, 128, -0.3, False),     # 432 query tiles; last tile 8 rows; negative scale
+    ("bf16", 1, 300, 1000, 128, None, False),  # 1200 query tiles, 16 key tiles each
+    ("bf16", 1, 300, 200, 128, None, False),   # 4 key tiles (every iteration a transition), 1 query tile per head
+    ("f16", 3, 100, 330, 64, 0.2, False),      # 6 key tiles (one plain iteration per tile), 2 query tiles per head
+    ("bf16", 2, 300, 1000, 64, None, True),    # causal: 8 query tiles per head (2 .. 16 key tiles), 2400 pairs
+    ("f16", 1, 600, 512, 64, -0.4, True),      # causal: 4 query tiles per head, negative scale
+    ("bf16", 4, 50, 700, 64, None, True),      # causal: 6 query tiles, ragged last tile (rows and keys)
+    ("bf16", 1, 520, 256, 64, None, True),     # causal: one pair per head, tiles of 2 and 4 key tiles
 ])
-def test_persistent_kernel(dtype, B, H, N, d, scale):
-    """Plain launches without a mask and with more query tiles than the
-    device has workgroup slots run the persistent kernel, which pipelines
-    across query tiles; it matches the oracle on every head, gives the same
-    bits as the per-tile kernel (the counters launch in launch_all), and
-    repeats bit for bit."""
+def test_persistent_kernel(dtype, B, H, N, d, scale, causal):
+    """Plain launches with more query tiles than the device has workgroup
+    slots run the persistent kernel (without a mask; causal at d = 64 with
+    an even number of query tiles), which pipelines across query tiles; it
+    matches the oracle on every head, gives the same bits as the per-tile
+    kernel (the counters launch in launch_all), and repeats bit for bit."""
     words = W.make_words((B, H, N, d), dtype, "normal", seed=21)
     s = W.scale_for(d) if scale is None else scale
-    _, (qd, kd, vd, o, lse, _) = check_against_oracle(words, dtype, False, s, what="persistent")
+    _, (qd, kd, vd, o, lse, _) = check_against_oracle(words, dtype, causal, s, what="persistent")
     for _ in range(2):
-        o2, l2 = fa.attention(qd, kd, vd, causal=False, scale=s)
+        o2, l2 = fa.attention(qd, kd, vd, causal=causal, scale=s)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
 

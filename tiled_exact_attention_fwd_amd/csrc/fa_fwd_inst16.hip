@@ -31,13 +31,19 @@ int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
                  : launch_kernel<Fwd16<T, FA_INST_D, C, false, false>>(p, stream);
 }
 
-#if FA_INST_C == 0
 #define FA_CAT4(a, b, c, d) a##b##c##d
 #define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
+#if FA_INST_C == 0
 // the persistent kernel (no mask, 16-bit output, no counters) on `grid` workgroups
 int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>::BQ == tile_q16(false), "grid tile");
     return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>>(p, stream, grid);
+}
+#elif FA_INST_D == 64
+// the causal persistent kernel (d = 64, 16-bit output, no counters)
+int FA_XCAT4(launch16pc_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
+    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>::BQ == tile_q16(true), "grid tile");
+    return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid);
 }
 #endif
 

@@ -775,7 +775,7 @@ struct Fwd16 {
 };
 
 // ---------------------------------------------------------------------------
-// Persistent 16-bit kernel without a mask (16-bit output, no counters).
+// Persistent 16-bit kernel (16-bit output, no counters).
 //
 // One workgroup per CU stays resident and takes the query tiles b, b + G,
 // b + 2 G, ... of the logical order above (G workgroups; with G a multiple
@@ -797,10 +797,17 @@ struct Fwd16 {
 //   j = nk - 1  the next tile's Q^T operands are read from that slice: the
 //               score MFMAs of this iteration start the next tile.
 // The host uses it for nk >= 4, where these are four different iterations.
+//
+// Causal variant (d = 64, two 128-row workgroups per CU): a query tile costs
+// its own number of key tiles, so a workgroup takes pairs of query tiles
+// (i, T - 1 - i) of a head, whose costs add up to the same for every pair.
+// The output has its own LDS slice, and the next tile's Q rows are copied
+// at j = 0, so that tiles of two key tiles (j = 0 and j = nk - 1 = 1) work;
+// the diagonal's masks fall on the last two key tiles of a query tile.
 // ---------------------------------------------------------------------------
-template <class T, int D>
+template <class T, int D, bool CAUSAL = false>
 struct Fwd16P {
-    using Bs = Fwd16<T, D, false, false, false>;
+    using Bs = Fwd16<T, D, CAUSAL, false, false>;
     static constexpr int WAVES = Bs::WAVES, BQ = Bs::BQ, OCC = Bs::OCC, NT = Bs::NT, BK = Bs::BK;
     static constexpr int RESIDENT = Bs::RESIDENT;
     static constexpr int ROWB = Bs::ROWB, TILEB = Bs::TILEB, NS = Bs::NS, NDB = Bs::NDB, NMB = Bs::NMB;
@@ -809,10 +816,15 @@ struct Fwd16P {
     static constexpr bool READ_FIRST = Bs::READ_FIRST;
     static constexpr int SLICE = 32 * ROWB;          // one wave's Q / O staging bytes
     static constexpr int QLOADS = SLICE / 1024;      // 16-byte copies per lane of a wave's Q rows
-    static constexpr int MIN_KEY_TILES = 4;
+    static constexpr bool SPLIT = CAUSAL;            // the output has its own staging slice
+    static constexpr int MIN_KEY_TILES = SPLIT ? 2 : 4;
+    static constexpr int QCOPY_AT = SPLIT ? 0 : 2;   // key tile at which the next Q rows are copied
+    static constexpr int STEADY_LO = SPLIT ? 2 : 3;  // plain iterations: STEADY_LO <= j <= nk - 3
     static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
     static constexpr int RPS = 64 / CPR;             // rows per 16-byte store
-    static_assert(RESIDENT == 1 && SLICE % 1024 == 0, "persistent shape");
+    static_assert(SLICE % 1024 == 0 && RESIDENT == (CAUSAL ? 2 : 1), "persistent shape");
+    static_assert((4 * TILEB + (SPLIT ? 2 : 1) * WAVES * SLICE) * RESIDENT <= 160 * 1024, "LDS per CU");
+    static_assert(!CAUSAL || BQ == 2 * BK, "causal masks on the last two key tiles");
 
     // The lane index, opaque to the optimiser: addresses derived from it in a
     // once-per-tile block are computed there, not hoisted out of the key loop
@@ -826,6 +838,7 @@ struct Fwd16P {
         size_t hoff;        // byte offset of the head in Q, K, V and O
         int hh;             // head (batch * H + h)
         int qt0;            // first query row
+        int nk;             // key tiles of the query tile
     };
 
     // Output of one query tile: acc / l rounded to 16 bits, staged in the
@@ -868,6 +881,7 @@ struct Fwd16P {
         // places first: their operand reads keep addresses below 64 KiB,
         // which the 16-bit offset field of an LDS instruction can reach)
         __shared__ __attribute__((aligned(256))) uint8_t qbuf[WAVES * SLICE];
+        __shared__ __attribute__((aligned(256))) uint8_t obuf[SPLIT ? WAVES * SLICE : 16];
         const int tid = threadIdx.x;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lane = tid & 63;
@@ -885,18 +899,39 @@ struct Fwd16P {
         const int total = pin_s(p.total);
 
         const int G = gridDim.x, b = blockIdx.x;
-        const int ntiles = (total - b + G - 1) / G;     // b < total
-        const int nk = (N + BK - 1) / BK;               // >= MIN_KEY_TILES
-        int gend = ntiles * nk;                         // key tiles of this workgroup
-        asm volatile("" : "+s"(gend));
+        // work units: query tiles, or (causal) pairs of query tiles; b < units
+        const int units = CAUSAL ? total / 2 : total;
+        const int ntiles = (CAUSAL ? 2 : 1) * ((units - b + G - 1) / G);
+        const int nk_all = (N + BK - 1) / BK;           // >= MIN_KEY_TILES
         const uint32_t head_bytes = (uint32_t)N * ROWB;
         uint8_t* const qslice = qbuf + wave * SLICE;
+        uint8_t* const oslice = SPLIT ? obuf + wave * SLICE : qslice;
 
         auto decode = [&](int k) {
-            const int L = xcd_remap(b + min(k, ntiles - 1) * G, total);
-            const int hh = L / tiles_q;
-            return TileInfo{(size_t)hh * head_bytes, hh, (L - hh * tiles_q) * BQ};
+            k = min(k, ntiles - 1);
+            int hh, qi;
+            if (CAUSAL) {
+                const int half = tiles_q / 2;
+                const int L = xcd_remap(b + (k >> 1) * G, units);
+                hh = L / half;
+                const int i = L - hh * half;
+                qi = (k & 1) ? i : tiles_q - 1 - i;
+            } else {
+                const int L = xcd_remap(b + k * G, units);
+                hh = L / tiles_q;
+                qi = L - hh * tiles_q;
+            }
+            const int qt0 = qi * BQ;
+            const int nkt = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk_all;
+            return TileInfo{(size_t)hh * head_bytes, hh, qt0, nkt};
         };
+        int gend = 0;                                   // key tiles of this workgroup
+        if (CAUSAL) {
+            for (int k = 0; k < ntiles; ++k) gend += decode(k).nk;
+        } else {
+            gend = ntiles * nk_all;
+        }
+        asm volatile("" : "+s"(gend));
         TileInfo cur = decode(0), nxt = decode(1), prv = cur;
 
         // zero fill before the first copy (see Fwd16)
@@ -965,10 +1000,11 @@ struct Fwd16P {
         // position of the softmax stream: key tile j0 of this workgroup's
         // query tile k0 (j0 = -1 before the first; j0 = nk until the wrap)
         int k0 = 0, j0 = -1;
-        // iterations with 3 <= j0 <= nk - 3 are plain: one range check, the
-        // copy sources advance by a tile; every other one recomputes its
-        // state in one block
-        const uint32_t nk_s = nk > 5 ? (uint32_t)(nk - 5) : 0u;
+        // iterations with STEADY_LO <= j0 <= nk - 3 are plain: one range
+        // check, the copy sources advance by a tile; every other one
+        // recomputes its state in one block
+        auto steady_count = [&](int nkt) { return nkt > STEADY_LO + 2 ? (uint32_t)(nkt - STEADY_LO - 2) : 0u; };
+        uint32_t nk_s = steady_count(cur.nk);
         const uint8_t* kc_ptr = kptr;      // K copy of this iteration (key tile g + 2)
         const uint8_t* vc_ptr = vptr;      // V copy (key tile g)
         uint32_t kc_ext = 0, vc_ext = 0;
@@ -985,14 +1021,14 @@ struct Fwd16P {
 
             __syncthreads();   // this wave's copies done (vmcnt 0), and everyone's
 
-            if ((uint32_t)(j0 - 3) >= nk_s) {
-                if (j0 == nk) {
+            if ((uint32_t)(j0 - STEADY_LO) >= nk_s) {
+                if (j0 == cur.nk) {
                     j0 = 0;
                     ++k0;
                 }
                 if (j0 == 1 && k0 >= 1) {
                     // the previous tile's output (no copy of this wave in flight)
-                    store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
+                    store_output(acc, inv_prev, oslice, out, prv, wave, lane, N);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
                 }
@@ -1006,8 +1042,9 @@ struct Fwd16P {
                     prv = cur;
                     cur = nxt;
                     nxt = decode(k0 + 1);
+                    nk_s = steady_count(cur.nk);
                 }
-                if (j0 == 2 && k0 + 1 < ntiles) {
+                if (j0 == QCOPY_AT && k0 + 1 < ntiles) {
                     // the next tile's Q rows into this wave's slice, chunks
                     // XOR-swizzled by row as the operand reads below expect
                     const uint32_t r0 = (uint32_t)(nxt.qt0 + wave * 32) * ROWB;
@@ -1022,7 +1059,7 @@ struct Fwd16P {
                             rq, (__attribute__((address_space(3))) void*)(qslice + u * 1024), 16, src, 0, 0, 0);
                     }
                 }
-                if (j0 == nk - 1 && k0 + 1 < ntiles) {
+                if (j0 == cur.nk - 1 && k0 + 1 < ntiles) {
                     // the score MFMAs of this iteration start the next tile
                     const int ol = opaque_lane(lane), oli = ol & 31, olh = ol >> 5;
                     const uint8_t* qs = qslice + oli * ROWB;
@@ -1032,11 +1069,13 @@ struct Fwd16P {
                         qreg[s] ^= qsign;
                     }
                 }
-                sm_on = j0 >= 0 && k0 < ntiles && cur.qt0 + wave * 32 < N;
+                const int q0w = cur.qt0 + wave * 32;
+                sm_on = j0 >= 0 && k0 < ntiles && q0w < N;
                 const int kk0 = j0 * BK;
-                if (sm_on && kk0 + BK > N) {
-                    // the ragged last key tile
-                    const int lim = N - 1 - kk0 - 8 * lh;
+                if (sm_on && ((CAUSAL && kk0 + BK - 1 > q0w) || kk0 + BK > N)) {
+                    // the diagonal and the ragged last key tile
+                    int lim = N - 1 - kk0 - 8 * lh;
+                    if (CAUSAL) lim = min(lim, q0w + li - kk0 - 8 * lh);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -1047,8 +1086,8 @@ struct Fwd16P {
                 }
                 // copy sources: K of key tile g + 2 and V of key tile g of the
                 // stream (empty extents outside it)
-                const bool kin = j0 + 2 < nk;
-                const uint32_t kcopy = g + 2 < gend ? (uint32_t)((kin ? j0 + 2 : j0 + 2 - nk) * TILEB) : head_bytes;
+                const bool kin = j0 + 2 < cur.nk;
+                const uint32_t kcopy = g + 2 < gend ? (uint32_t)((kin ? j0 + 2 : j0 + 2 - cur.nk) * TILEB) : head_bytes;
                 const uint32_t vcopy = j0 >= 0 && g < gend ? (uint32_t)(j0 * TILEB) : head_bytes;
                 kc_ptr = kptr + (kin ? cur.hoff : nxt.hoff) + kcopy;
                 kc_ext = head_bytes - kcopy;

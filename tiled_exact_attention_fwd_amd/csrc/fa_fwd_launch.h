@@ -39,6 +39,9 @@ int launch16p_bf16_d128(const FwdParams& p, int grid, void* stream);
 int launch16p_f16_d64(const FwdParams& p, int grid, void* stream);
 int launch16p_f16_d128(const FwdParams& p, int grid, void* stream);
 constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TILES; }
+// causal persistent kernels (d = 64; an even number of query tiles, paired)
+int launch16pc_bf16_d64(const FwdParams& p, int grid, void* stream);
+int launch16pc_f16_d64(const FwdParams& p, int grid, void* stream);
 int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
 int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
 
