@@ -777,9 +777,10 @@ struct Fwd16 {
 // ---------------------------------------------------------------------------
 // Persistent 16-bit kernel (16-bit output, no counters).
 //
-// One workgroup per CU stays resident and takes the query tiles b, b + G,
-// b + 2 G, ... of the logical order above (G workgroups; with G a multiple
-// of 8 every tile of a workgroup lies on its XCD's range).  Its waves run
+// One workgroup per workgroup slot of the device (one per CU without a
+// mask) stays resident and takes the query tiles b, b + G, b + 2 G, ... of
+// the logical order above (G workgroups; with G a multiple of 8 every tile
+// of a workgroup lies on its XCD's range).  Its waves run
 // the key loops of those tiles back to back as one stream of key tiles, so
 // the software pipeline of Fwd16 neither drains nor refills between query
 // tiles: while the output MFMAs finish a tile's last key tile, the score
@@ -796,7 +797,8 @@ struct Fwd16 {
 //               loads into the wave's own staging slice);
 //   j = nk - 1  the next tile's Q^T operands are read from that slice: the
 //               score MFMAs of this iteration start the next tile.
-// The host uses it for nk >= 4, where these are four different iterations.
+// Without a mask the host uses it for nk >= 4, where these are four
+// different iterations.
 //
 // Causal variant (d = 64, two 128-row workgroups per CU): a query tile costs
 // its own number of key tiles, so a workgroup takes pairs of query tiles
