@@ -284,6 +284,36 @@ def test_persistent_kernel(dtype, B, H, N, d, scale, causal):
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
 
 
+@pytest.mark.parametrize("shape,causal", [((2, 160, 1000, 64), False),   # persistent kernel
+                                          ((2, 300, 1000, 64), True),    # causal persistent kernel
+                                          ((1, 8, 2048, 128), True)])    # per-tile kernel
+def test_graph_replay(shape, causal):
+    """A launch captured into a HIP graph replays to the bits of the eager
+    launch, three times, with eager launches and fills in between."""
+    words = W.make_words(shape, "bf16", "normal", seed=31)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    s = W.scale_for(shape[3])
+    o_ref, l_ref = fa.attention(qd, kd, vd, causal=causal, scale=s)
+    o, lse = torch.empty_like(o_ref), torch.empty_like(l_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.attention(qd, kd, vd, causal=causal, scale=s, o=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.attention(qd, kd, vd, causal=causal, scale=s, o=o, lse=lse)
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref), r
+        fa.attention(qd, kd, vd, causal=causal, scale=s)
+        torch.cuda.synchronize()
+
+
 def test_guard_bands_untouched():
     """Ragged N: nothing is written outside o and lse."""
     B, H, N, d = 3, 5, 1000, 64
