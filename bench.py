@@ -16,6 +16,13 @@ over a bounded sample of the same workload.
 
 --profile-run launches a copy kernel of known size and then the forward a few
 times, without timing, for rocprofv3 counter collection (HBM bytes).
+
+--sweep times the same non-causal bf16 workload at every tile shape of the
+tile-size sweep (query rows x keys in {64, 128, 256} x {32, 64, 128}, the
+per-tile kernel of each shape) and prints a table with each kernel's
+registers, spills, LDS bytes and occupancy beside the working set of
+"FlashAttention Memory Model" Q3 (Q, K, V, O and S tiles in 16 bits).
+--summarize l2 DIR reads a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run of it.
 """
 
 import argparse
@@ -201,6 +208,19 @@ def summarize(kind, paths):
             print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {tail_avg} |")
         return
+    if kind == "l2":
+        hits, misses = {}, {}
+        for r in rows(paths[0], "*counter_collection.csv"):
+            dst = hits if r["Counter_Name"] == "TCC_HIT_sum" else misses
+            dst.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        print("| kernel | dispatches | L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) |")
+        print("|---|---|---|")
+        for name in sorted(hits):
+            if "fa::" not in name:
+                continue
+            h, m = statistics.median(hits[name]), statistics.median(misses.get(name, [0.0]))
+            print(f"| {name} | {len(hits[name])} | {h / (h + m):.3f} |")
+        return
     per = {}
     for d in paths:
         for r in rows(d, "*counter_collection.csv"):
@@ -248,6 +268,61 @@ def profile_run():
         print(f"{name} causal={causal}: {r}", flush=True)
 
 
+SWEEP_TILES = [(64, 32), (64, 64), (64, 128), (128, 32), (128, 64), (128, 128),
+               (256, 32), (256, 64), (256, 128)]
+
+
+def sweep_kernel_key(tq, tk):
+    """Mangled-name fragment of the plain per-tile kernel of one sweep shape."""
+    waves = 0 if (tq, tk) == (256, 64) else tq // 32
+    return f"Fwd16INS_4BF16ELi128ELb0ELb0ELb0ELi{waves}ELi{tk}E"
+
+
+def tile_sweep(steps, warmup):
+    """Tile-size sweep at the C2b shape: TFLOP/s and kernel resources per shape."""
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    from tiled_exact_attention_fwd_amd import codeobj
+    wl = W.WORKLOADS["C2b"]
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    q, k, v = (upload(w, wl.dtype) for w in words)
+    o = torch.empty_like(q)
+    lse = torch.empty(wl.shape[:3], dtype=torch.float32, device=q.device)
+    B, H, N, d = wl.shape
+    handle = torch.cuda.current_stream().cuda_stream
+    res = codeobj.kernel_resources(fa.LIB_PATH)
+    print(f"| tile (query rows x keys) | TFLOP/s | % of peak | VGPR (arch+acc) | spilled VGPRs | "
+          f"LDS bytes | waves per SIMD | working set, 16-bit tiles (bytes) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for tq, tk in SWEEP_TILES:
+        def launch():
+            st = fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              B, H, N, d, W.scale_for(d), 0, handle, fa.FA_DTYPE_BF16, tile_q=tq, tile_k=tk)
+            if st != fa.FA_OK:
+                raise RuntimeError(f"fa_fwd_ex {tq}x{tk}: {fa.fa_strerror(st)}")
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        tf = wl.flops(False) / (e0.elapsed_time(e1) / steps * 1e-3) / 1e12
+        key = sweep_kernel_key(tq, tk)
+        r = next(v_ for n_, v_ in res.items() if key in n_)
+        waves = tq // 32
+        # waves per SIMD: the launch bound (2), the register file (512 per
+        # lane), and the LDS (160 KiB per CU, shared by the workgroups)
+        regs = -(-r["vgpr"] // 8) * 8
+        occ = min(2, 512 // regs, (160 * 1024 // r["lds"]) * waves / 4)
+        ws = (2 * tq * d + 2 * tk * d + tq * tk) * 2
+        print(f"| {tq} x {tk} | {tf:.1f} | {100 * tf / PEAK_TFLOPS['bf16']:.1f}% | {r['vgpr']} | "
+              f"{r['vgpr_spill']} | {r['lds']} | {occ:g} | {ws} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,9 +332,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="tile-size sweep table")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
-                         "'trace DIR [STEPS]' or 'counters FETCH_DIR WRITE_DIR'")
+                         "'trace DIR [STEPS]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
     a = ap.parse_args()
     if a.summarize:
         summarize(a.summarize[0], a.summarize[1:])
@@ -278,6 +354,9 @@ def main():
         sys.exit(2)
     if a.profile_run:
         profile_run()
+        return
+    if a.sweep:
+        tile_sweep(a.steps, a.warmup)
         return
 
     wl = W.WORKLOADS["C2b"]

@@ -110,8 +110,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   out_dtype  0: o has the input element type; 1: o is fp32 (the output is
  *              then not rounded to 16 bits -- used to check the kernel's
  *              arithmetic separately from the final rounding)
- *   tile_q, tile_k  0 selects the library default; otherwise the shape must
- *              be one that was built (see fa_fwd_tile_shape)
+ *   tile_q, tile_k  0 selects the library default (see fa_fwd_tile_shape);
+ *              otherwise the shape must be one that was built: the default,
+ *              or for bf16, d = 128, no mask and 16-bit output any of
+ *              tile_q in {64, 128, 256} x tile_k in {32, 64, 128} (a tile-size
+ *              sweep after "FlashAttention Memory Model" Q3, the tile-size
+ *              trade-off; a launch that names one of these shapes, the
+ *              default included, uses the per-tile kernel of that shape).
+ *              FA_ERR_UNSUPPORTED otherwise.
  *   counters   NULL for the plain kernel; otherwise a device array of
  *              FA_NUM_COUNTERS unsigned 64-bit integers to which the launch
  *              ADDS its tile counts (indices above).  The caller zeroes it.

@@ -105,6 +105,19 @@ def test_ex_argument_checks():
     assert ex(tile_q=32, tile_k=64) == fa.FA_ERR_UNSUPPORTED
     assert ex(tile_q=-1) == fa.FA_ERR_INVALID
     assert fa.lib().fa_fwd_ex(None) == fa.FA_ERR_INVALID
+    # the tile-size sweep shapes exist for bf16, d = 128, no mask, 16-bit output only
+    sweep = dict(dtype=fa.FA_DTYPE_BF16, d=128)
+    passes_checks = (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)   # no GPU here
+    for tq in (64, 128, 256):
+        for tk in (32, 64, 128):
+            assert ex(tile_q=tq, tile_k=tk, **sweep) in passes_checks
+            assert ex(tile_q=tq, tile_k=tk, causal=1, **sweep) in ((fa.FA_ERR_UNSUPPORTED,) if (tq, tk) != (128, 64)
+                                                                   else passes_checks)
+            assert ex(tile_q=tq, tile_k=tk, out_dtype=1, **sweep) in ((fa.FA_ERR_UNSUPPORTED,) if (tq, tk) != (256, 64)
+                                                                      else passes_checks)
+    assert ex(tile_q=128, tile_k=32, dtype=fa.FA_DTYPE_F16, d=128) == fa.FA_ERR_UNSUPPORTED
+    assert ex(tile_q=128, tile_k=32, dtype=fa.FA_DTYPE_BF16, d=64) == fa.FA_ERR_UNSUPPORTED
+    assert ex(tile_q=512, tile_k=64, **sweep) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_per_dtype_entry_points_share_validation():

@@ -9,53 +9,21 @@ results during development, and the kernels are written to avoid both:
 * a scalar-memory load writing an SGPR that such an in-flight copy reads
   (its buffer resource or M0 source).
 
-The code object is taken from ``libfa_fwd.so`` (the offload bundles in its
-``.hip_fatbin`` section) and disassembled with the ROCm llvm-objdump; every
+The code objects are taken from ``libfa_fwd.so`` (``codeobj.code_objects``)
+and disassembled with the ROCm llvm-objdump; every
 kernel is scanned in layout order, which is conservative across branches.
 """
 
 import os
 import re
-import struct
 import subprocess
 
 import pytest
 
+from tiled_exact_attention_fwd_amd.codeobj import LLVM, code_objects
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "tiled_exact_attention_fwd_amd", "libfa_fwd.so")
-LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
-MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
-
-
-def _section(path, name):
-    """Bytes of an ELF64 section, by name (minimal reader)."""
-    data = open(path, "rb").read()
-    shoff, = struct.unpack_from("<Q", data, 0x28)
-    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
-    hdrs = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
-    stroff = hdrs[shstrndx][4]
-    for h in hdrs:
-        end = data.index(b"\0", stroff + h[0])
-        if data[stroff + h[0]:end].decode() == name:
-            return data[h[4]:h[4] + h[5]]
-    raise KeyError(name)
-
-
-def _code_objects(fatbin):
-    """gfx950 ELF code objects of every offload bundle in the section."""
-    out = []
-    pos = fatbin.find(MAGIC)
-    while pos >= 0:
-        n, = struct.unpack_from("<Q", fatbin, pos + len(MAGIC))
-        q = pos + len(MAGIC) + 8
-        for _ in range(n):
-            off, size, tlen = struct.unpack_from("<QQQ", fatbin, q)
-            triple = fatbin[q + 24:q + 24 + tlen].decode()
-            q += 24 + tlen
-            if "amdgcn" in triple and "gfx950" in triple:
-                out.append(fatbin[pos + off:pos + off + size])
-        pos = fatbin.find(MAGIC, pos + 1)
-    return out
 
 
 def _sgprs(tok):
@@ -111,7 +79,7 @@ def test_no_lds_write_or_smem_overwrite_during_lds_copies(tmp_path):
     objdump = os.path.join(LLVM, "llvm-objdump")
     if not os.path.exists(objdump):
         pytest.skip("llvm-objdump not available")
-    cos = _code_objects(_section(LIB, ".hip_fatbin"))
+    cos = code_objects(LIB)
     assert cos, "no gfx950 code object in the library"
     kernels = 0
     problems = {}

@@ -314,6 +314,33 @@ def test_graph_replay(shape, causal):
         torch.cuda.synchronize()
 
 
+SWEEP_TILES = [(64, 32), (64, 64), (64, 128), (128, 32), (128, 64), (128, 128), (256, 32), (256, 128)]
+
+
+@pytest.mark.parametrize("tile", SWEEP_TILES)
+def test_tile_sweep_shapes(tile):
+    """Every tile-size sweep shape (bf16, d = 128, no mask) matches the oracle
+    over several query and key tiles with ragged N, counts its tiles as the
+    oracle's block counts at that shape, and its counting kernel computes the
+    same bits as its plain one."""
+    B, H, N, d = 1, 3, 300, 128
+    words = W.make_words((B, H, N, d), "bf16", "normal", seed=41)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    s = W.scale_for(d)
+    o, lse = fa.attention(qd, kd, vd, scale=s, tile=tile)
+    oc, lsec, cnt = fa.attention(qd, kd, vd, scale=s, tile=tile, counters=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), oc.view(torch.int16)) and torch.equal(lse, lsec)
+    c = oracle.block_counts(N, tile[0], tile[1], False)
+    assert cnt == {k_: v_ * B * H for k_, v_ in c.items()}, cnt
+    o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        vals = [W.decode64(w[0, h], "bf16")[None, None] for w in words]
+        o_ref, lse_ref = oracle.attention_ref(*vals, s, False)
+        errs = gate_errors(None, o_np[0, h][None, None], lse_np[0, h][None, None], o_ref, lse_ref, "bf16")
+        assert_gates(errs, "bf16", f"tile {tile} head {h}")
+
+
 def test_guard_bands_untouched():
     """Ragged N: nothing is written outside o and lse."""
     B, H, N, d = 3, 5, 1000, 64

@@ -135,13 +135,15 @@ def dtype_code(torch_dtype):
 
 
 def attention(q, k, v, causal=False, scale=None, out_f32=False, counters=False,
-              o=None, lse=None, stream=None):
+              o=None, lse=None, stream=None, tile=None):
     """Exact attention forward on the device.
 
     q, k, v: contiguous [B, H, N, d] CUDA(HIP) tensors of one dtype (fp32, fp16
     or bf16).  Returns ``(o, lse)``, or ``(o, lse, counts)`` with ``counts`` a
     dict of tile counts when ``counters`` is set (that launch uses the
     instrumented kernel).  ``o`` / ``lse`` may be passed in preallocated.
+    ``tile`` = (query rows, keys) asks for a tile shape other than the
+    default (bf16, d = 128, no mask: {64, 128, 256} x {32, 64, 128}).
     """
     import math
     import torch
@@ -166,6 +168,7 @@ def attention(q, k, v, causal=False, scale=None, out_f32=False, counters=False,
     st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                    B, H, N, d, float(scale), int(bool(causal)), stream, dt,
                    out_dtype=1 if out_f32 else 0,
+                   tile_q=tile[0] if tile else 0, tile_k=tile[1] if tile else 0,
                    counters=cnt.data_ptr() if cnt is not None else None)
     if st == FA_ERR_INVALID:
         raise ValueError(f"fa_fwd: {fa_strerror(st)}")

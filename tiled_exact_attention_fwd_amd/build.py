@@ -38,6 +38,11 @@ for t in ("bf16", "f16"):
                           [f"-DFA_INST_T={t}", f"-DFA_INST_D={d}", f"-DFA_INST_C={c}"]))
 for c in (0, 1):
     UNITS.append((f"inst32_c{c}", "fa_fwd_inst32.hip", [f"-DFA_INST_C={c}"]))
+# tile-size sweep shapes (bf16, d = 128, no mask)
+for tq in (64, 128, 256):
+    for tk in (32, 64, 128):
+        if (tq, tk) != (256, 64):
+            UNITS.append((f"inst16t_q{tq}_k{tk}", "fa_fwd_inst16_tiles.hip", [f"-DFA_TQ={tq}", f"-DFA_TK={tk}"]))
 
 
 def hipcc():

@@ -34,10 +34,28 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Default (and only built) tile shape per element type, head dimension and mask.
+// Default tile shape per element type, head dimension and mask.
 void tile_shape(int dtype, int d, int causal, int* tq, int* tk) {
     if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
     else { *tq = fa::tile_q16(causal != 0); *tk = 64; }
+}
+
+// The tile-size sweep shapes: bf16, d = 128, no mask, 16-bit output,
+// (query rows, keys) in {64, 128, 256} x {32, 64, 128}.
+bool sweep_shape(const fa_fwd_args* a, int tq, int tk) {
+    return a->dtype == FA_DTYPE_BF16 && a->d == 128 && !a->causal && !a->out_dtype &&
+           (tq == 64 || tq == 128 || tq == 256) && (tk == 32 || tk == 64 || tk == 128);
+}
+
+// The shape a launch uses: the default, or the one it asks for.
+int launch_shape(const fa_fwd_args* a, int* tq, int* tk) {
+    tile_shape(a->dtype, a->d, a->causal, tq, tk);
+    if (a->tile_q < 0 || a->tile_k < 0) return FA_ERR_INVALID;
+    const int rq = a->tile_q ? a->tile_q : *tq, rk = a->tile_k ? a->tile_k : *tk;
+    if ((rq != *tq || rk != *tk) && !sweep_shape(a, rq, rk)) return FA_ERR_UNSUPPORTED;
+    *tq = rq;
+    *tk = rk;
+    return FA_OK;
 }
 
 int check_args(const fa_fwd_args* a) {
@@ -51,9 +69,8 @@ int check_args(const fa_fwd_args* a) {
         return FA_ERR_UNSUPPORTED;
     if (a->d != 64 && a->d != 128) return FA_ERR_UNSUPPORTED;
     int tq, tk;
-    tile_shape(a->dtype, a->d, a->causal, &tq, &tk);
-    if (a->tile_q < 0 || a->tile_k < 0) return FA_ERR_INVALID;
-    if ((a->tile_q && a->tile_q != tq) || (a->tile_k && a->tile_k != tk)) return FA_ERR_UNSUPPORTED;
+    const int ts = launch_shape(a, &tq, &tk);
+    if (ts != FA_OK) return ts;
     const int e = elem_size(a->dtype);
     if ((uint64_t)a->N * a->d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;   // per-head bytes
     const uint64_t tiles = (uint64_t)a->B * a->H * (uint64_t)((a->N + tq - 1) / tq);
@@ -94,8 +111,9 @@ int run(const fa_fwd_args* a) {
     st = check_device(&cus);
     if (st != FA_OK) return st;
 
-    int tq, tk;
-    tile_shape(a->dtype, a->d, a->causal, &tq, &tk);
+    int tq, tk, dq, dk;
+    launch_shape(a, &tq, &tk);
+    tile_shape(a->dtype, a->d, a->causal, &dq, &dk);
     FwdParams p;
     p.q = a->q;
     p.k = a->k;
@@ -117,6 +135,23 @@ int run(const fa_fwd_args* a) {
     const bool count = a->counters != nullptr;
 
     const int c = a->causal, o32 = a->out_dtype;
+    if (a->tile_q && sweep_shape(a, tq, tk)) {
+        // an explicitly requested tile-size sweep shape: the per-tile kernel
+        // of that shape (for the default shape too, so that a sweep compares
+        // one kernel family)
+        switch (tq * 1000 + tk) {
+        case 256064: return fa::launch16_bf16_d128_c0(p, 0, count, a->stream);
+        case 64032: return fa::launch16t_q64_k32(p, count, a->stream);
+        case 64064: return fa::launch16t_q64_k64(p, count, a->stream);
+        case 64128: return fa::launch16t_q64_k128(p, count, a->stream);
+        case 128032: return fa::launch16t_q128_k32(p, count, a->stream);
+        case 128064: return fa::launch16t_q128_k64(p, count, a->stream);
+        case 128128: return fa::launch16t_q128_k128(p, count, a->stream);
+        case 256032: return fa::launch16t_q256_k32(p, count, a->stream);
+        case 256128: return fa::launch16t_q256_k128(p, count, a->stream);
+        default: return FA_ERR_UNSUPPORTED;
+        }
+    }
     // A plain 16-bit launch without a mask that has more query tiles than
     // the device has workgroup slots runs the persistent kernel: one
     // workgroup per slot (a multiple of 8, so that each keeps to one XCD's

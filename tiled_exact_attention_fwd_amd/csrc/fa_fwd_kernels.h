@@ -290,7 +290,10 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT>
+// WQ (waves per workgroup, 0 = the default below) and BKT (keys per tile)
+// select other tile shapes; the library builds the defaults for every type
+// and a tile-size sweep (bf16, d = 128, no mask) besides.
+template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT, int WQ = 0, int BKT = 64>
 struct Fwd16 {
     // Eight waves (256 query rows, one workgroup per CU) share each K / V
     // tile copy without a mask: half the L2 -> LDS traffic of four.  Causal
@@ -298,12 +301,12 @@ struct Fwd16 {
     // waves' work differs along the diagonal, and a smaller workgroup waits
     // less at its barriers for the wave with the most keys (under the
     // longest-first tile order eight waves measure the same).
-    static constexpr int WAVES = CAUSAL ? 4 : 8;
+    static constexpr int WAVES = WQ ? WQ : (CAUSAL ? 4 : 8);
     static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
     static constexpr int OCC = 2;                  // waves per SIMD
     static constexpr int RESIDENT = 4 * OCC / WAVES;   // workgroups per CU
     static constexpr int NT = 64 * WAVES;
-    static constexpr int BK = 64;                  // keys per tile
+    static constexpr int BK = BKT;                 // keys per tile
     static constexpr int ROWB = 2 * D;             // bytes per K / V row
     static constexpr int TILEB = BK * ROWB;        // bytes per K or V tile
     static constexpr int NS = D / 16;              // k-steps of K Q^T per 32-key block
@@ -337,13 +340,14 @@ struct Fwd16 {
         int voff[NDB];      // V^T operand byte offsets within a tile, per d block
     };
 
-    // Per-lane source offset (within a tile) of this lane's 16-byte copies:
-    // the copies of a thread are 4 KiB apart in LDS, i.e. a multiple of 16
-    // rows apart, which leaves the swizzle of the row unchanged; so one offset
-    // serves all of them.
+    // Per-lane source offset (within a tile) of this lane's u-th 16-byte
+    // copy.  A thread's copies are WAVES KiB apart in LDS; when that is a
+    // multiple of 16 rows (every default shape) the swizzle of the row is the
+    // same for all of them and one offset serves all.
+    static constexpr bool SAME_SWIZZLE = (WAVES * 1024 / ROWB) % 16 == 0;
     template <bool ISK>
-    static __device__ __forceinline__ uint32_t copy_offset(int wave, int lane) {
-        const int off = wave * 1024 + lane * 16;
+    static __device__ __forceinline__ uint32_t copy_offset(int wave, int lane, int u = 0) {
+        const int off = (u * WAVES + wave) * 1024 + lane * 16;
         const int row = off / ROWB, pos = (off % ROWB) >> 4;
         const int chunk = pos ^ (ISK ? fk(row) : fv(row));
         return (uint32_t)(row * ROWB + chunk * 16);
@@ -589,8 +593,13 @@ struct Fwd16 {
         uint32_t koff_c[LOADS], voff_c[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-            koff_c[u] = ksrc + (uint32_t)(u * WAVES * 1024);
-            voff_c[u] = vsrc + (uint32_t)(u * WAVES * 1024);
+            if constexpr (SAME_SWIZZLE) {
+                koff_c[u] = ksrc + (uint32_t)(u * WAVES * 1024);
+                voff_c[u] = vsrc + (uint32_t)(u * WAVES * 1024);
+            } else {
+                koff_c[u] = copy_offset<true>(wave, lane, u);
+                voff_c[u] = copy_offset<false>(wave, lane, u);
+            }
         }
 
         // prologue: K_0 into kbuf0
@@ -738,20 +747,21 @@ struct Fwd16 {
                                        acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv});
                     }
             }
-        } else {
+        } else if constexpr (WAVES * 32 * ROWB <= 4 * TILEB) {
             // The 16-bit output leaves through LDS so that every store writes
             // whole rows (stored straight from the registers, each store
             // would scatter 8-byte pieces over 32 rows).  The barrier frees
             // the K / V buffers: every wave has passed its last read and its
             // copies have landed.  Each wave stages its 32 rows in its own
-            // half of one buffer, 16-byte chunks XOR-swizzled by row against
-            // bank conflicts, then stores 16 bytes per lane, CPR lanes per row.
+            // slice of them, 16-byte chunks XOR-swizzled by row against bank
+            // conflicts, then stores 16 bytes per lane, CPR lanes per row.
             constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
             constexpr int RPS = 64 / CPR;               // rows per store
-            static_assert(2 * 32 * ROWB <= TILEB && WAVES <= 8, "output staging");
+            constexpr int SLICE = 32 * ROWB;
+            static_assert(TILEB % SLICE == 0, "output staging");
             __syncthreads();
-            const int sb = wave >> 1;
-            uint8_t* const ost = (sb == 0 ? kbuf0 : sb == 1 ? kbuf1 : sb == 2 ? vbuf0 : vbuf1) + (wave & 1) * 32 * ROWB;
+            const int sb = wave * SLICE / TILEB;
+            uint8_t* const ost = (sb == 0 ? kbuf0 : sb == 1 ? kbuf1 : sb == 2 ? vbuf0 : vbuf1) + (wave * SLICE) % TILEB;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -767,6 +777,21 @@ struct Fwd16 {
                 const int r = i * RPS + lane / CPR, c = lane % CPR;
                 const u32x4_t v = *(const u32x4_t*)(ost + r * ROWB + ((c ^ (r % CPR)) << 4));
                 if (q0w + r < N) gstore((uint16_t*)out + head_elems + (size_t)(q0w + r) * D + 8 * c, v);
+            }
+        } else {
+            // (tile shapes whose K / V buffers cannot hold every wave's rows:
+            // 8-byte pieces straight from the registers)
+            if (qrow < N) {
+                const size_t orow = head_elems + (size_t)qrow * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int d0 = 32 * db + 8 * jj + 4 * lh;
+                        const float o0 = acc[db][4 * jj + 0] * inv, o1 = acc[db][4 * jj + 1] * inv;
+                        const float o2 = acc[db][4 * jj + 2] * inv, o3 = acc[db][4 * jj + 3] * inv;
+                        gstore((uint16_t*)out + orow + d0, u32x2_t{pack2<T>(o0, o1), pack2<T>(o2, o3)});
+                    }
             }
         }
         if (lh == 0 && qrow < N) gstore(lse + (size_t)hh * N + qrow, (st.mc + __log2f(l)) * kLn2);

@@ -42,6 +42,18 @@ constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TIL
 // causal persistent kernels (d = 64; an even number of query tiles, paired)
 int launch16pc_bf16_d64(const FwdParams& p, int grid, void* stream);
 int launch16pc_f16_d64(const FwdParams& p, int grid, void* stream);
+// tile-size sweep (bf16, d = 128, no mask): every (query rows, keys) in
+// {64, 128, 256} x {32, 64, 128} besides the default 256 x 64
+#define FA_DECLARE_TILE(Q, K) int launch16t_q##Q##_k##K(const FwdParams& p, bool count, void* stream);
+FA_DECLARE_TILE(64, 32)
+FA_DECLARE_TILE(64, 64)
+FA_DECLARE_TILE(64, 128)
+FA_DECLARE_TILE(128, 32)
+FA_DECLARE_TILE(128, 64)
+FA_DECLARE_TILE(128, 128)
+FA_DECLARE_TILE(256, 32)
+FA_DECLARE_TILE(256, 128)
+#undef FA_DECLARE_TILE
 int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
 int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
 
