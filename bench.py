@@ -23,6 +23,11 @@ per-tile kernel of each shape) and prints a table with each kernel's
 registers, spills, LDS bytes and occupancy beside the working set of
 "FlashAttention Memory Model" Q3 (Q, K, V, O and S tiles in 16 bits).
 --summarize l2 DIR reads a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run of it.
+
+--standard times the standard forward of include/fa_standard.h (S and P
+materialised in HBM) on the same workload, after the copy kernel of
+--profile-run, so that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of it give
+its HBM bytes per kernel for comparison with the tiled forward.
 """
 
 import argparse
@@ -252,10 +257,10 @@ def summarize(kind, paths):
               f"{statistics.median(vals) * 1024 * scale / (1 << 20):.2f} MiB scaled |")
 
 
-def profile_run():
-    """Copy kernel of known size (counter calibration), then the forward."""
+def copy_calibration():
+    """Copy kernel of known size: what FETCH_SIZE / WRITE_SIZE read for it
+    scales the counters of the other kernels."""
     import torch
-    import fa_workloads as W
     src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
     src.fill_(1.0)
     dst = torch.empty_like(src)
@@ -263,9 +268,52 @@ def profile_run():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"copy kernel: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written", flush=True)
+
+
+def profile_run():
+    """Copy kernel of known size (counter calibration), then the forward."""
+    import fa_workloads as W
+    copy_calibration()
     for name, causal in (("C2b", False), ("C3", True)):
         r = time_workload(W.WORKLOADS[name], causal, 3, 1)
         print(f"{name} causal={causal}: {r}", flush=True)
+
+
+def standard_baseline(steps, warmup):
+    """The standard forward (S and P in HBM) on the C2b workload."""
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    copy_calibration()
+    wl = W.WORKLOADS["C2b"]
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    q, k, v = (upload(w, wl.dtype) for w in words)
+    B, H, N, d = wl.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    sm = torch.empty((B, H, N, N), dtype=q.dtype, device=q.device)
+    pm = torch.empty_like(sm)
+    handle = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        st = fa.fa_standard_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                sm.data_ptr(), pm.data_ptr(), B, H, N, d, W.scale_for(d), 0, handle,
+                                fa.FA_DTYPE_BF16)
+        if st != fa.FA_OK:
+            raise RuntimeError(f"fa_standard_fwd: {fa.fa_strerror(st)}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"standard_forward": "S and P materialised", "workload": "B=4 H=16 N=4096 d=128 bf16 non-causal",
+                      "ms_per_step": round(ms, 4), "TFLOP/s": round(wl.flops(False) / (ms * 1e-3) / 1e12, 2),
+                      "S_and_P_bytes": 2 * B * H * N * N * 2}), flush=True)
 
 
 SWEEP_TILES = [(64, 32), (64, 64), (64, 128), (128, 32), (128, 64), (128, 128),
@@ -333,6 +381,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="tile-size sweep table")
+    ap.add_argument("--standard", action="store_true", help="time the standard (materialising) forward")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
                          "'trace DIR [STEPS]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
@@ -357,6 +406,9 @@ def main():
         return
     if a.sweep:
         tile_sweep(a.steps, a.warmup)
+        return
+    if a.standard:
+        standard_baseline(a.steps, a.warmup)
         return
 
     wl = W.WORKLOADS["C2b"]

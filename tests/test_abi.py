@@ -1,5 +1,5 @@
 """The C-ABI library without a GPU: it loads, exports every function that
-include/fa_fwd.h declares, and rejects bad arguments before any HIP call
+include/*.h declares, and rejects bad arguments before any HIP call
 (sizes must be positive, as the memory-model page's helpers require; null
 pointers; bad flags; overlapping outputs; unsupported shapes)."""
 
@@ -11,22 +11,25 @@ import pytest
 
 import tiled_exact_attention_fwd_amd as fa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fa_fwd.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 # fake, well separated device addresses: validation never dereferences them
 Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.lib()
     names = declared_functions()
-    assert len(names) >= 8
+    assert len(names) >= 9 and "fa_standard_fwd" in names
     for n in names:
         assert hasattr(lib, n), n
         assert n in fa.SIGNATURES, f"binding lacks {n}"
@@ -118,6 +121,25 @@ def test_ex_argument_checks():
     assert ex(tile_q=128, tile_k=32, dtype=fa.FA_DTYPE_F16, d=128) == fa.FA_ERR_UNSUPPORTED
     assert ex(tile_q=128, tile_k=32, dtype=fa.FA_DTYPE_BF16, d=64) == fa.FA_ERR_UNSUPPORTED
     assert ex(tile_q=512, tile_k=64, **sweep) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_standard_argument_checks():
+    S, P = 0x60000000, 0x70000000
+
+    def std(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, s=S, p=P, B=1, H=1, N=256, d=64, scale=0.125, causal=0,
+                 stream=None, dtype=fa.FA_DTYPE_BF16)
+        a.update(over)
+        return fa.fa_standard_fwd(**a)
+    assert std(B=0) == fa.FA_ERR_INVALID
+    assert std(N=-1) == fa.FA_ERR_INVALID
+    assert std(s=None) == fa.FA_ERR_INVALID
+    assert std(p=P + 8) == fa.FA_ERR_INVALID              # not 16-byte aligned
+    assert std(causal=2) == fa.FA_ERR_INVALID
+    assert std(scale=float("nan")) == fa.FA_ERR_INVALID
+    assert std(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert std(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert std(N=1 << 23, d=128) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_per_dtype_entry_points_share_validation():

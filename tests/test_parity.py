@@ -341,6 +341,45 @@ def test_tile_sweep_shapes(tile):
         assert_gates(errs, "bf16", f"tile {tile} head {h}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [200, 257])
+def test_standard_baseline(dtype, d, causal, N):
+    """The standard forward (S and P materialised in HBM, fa_standard_fwd):
+    O passes the same gate against the oracle, and LSE the bound that S's
+    16-bit rounding allows; S is scale Q K^T and each row of P the softmax
+    of the stored S, within their 16-bit rounding; P is 0 above the diagonal
+    under the causal mask."""
+    B, H = 1, 2
+    words = W.make_words((B, H, N, d), dtype, "normal", seed=51)
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    sc = W.scale_for(d)
+    o, lse, s_dev, p_dev = fa.standard_attention(qd, kd, vd, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
+    s_np, p_np = out_to64(s_dev), out_to64(p_dev)
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    vis = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    for h in range(H):
+        vals = [W.decode64(w[0, h], dtype) for w in words]
+        o_ref, lse_ref = oracle.attention_ref(*(x[None, None] for x in vals), sc, causal)
+        errs = gate_errors(None, o_np[0, h][None, None], lse_np[0, h][None, None], o_ref, lse_ref, dtype)
+        assert errs["g2"] <= TOL_O[dtype], errs
+        s_ref = float(np.float32(sc)) * (vals[0] @ vals[1].T)
+        # LSE from the 16-bit S: d LSE / d S_j = P_j, so the error is at most
+        # the largest rounding error of the row's visible S: half an ulp,
+        # at most |S| 2^-(m+1) with m mantissa bits (bf16 7, fp16 10)
+        bound = rel * np.abs(np.where(vis, s_ref, 0.0)).max(axis=1) + 1e-5
+        assert np.all(np.abs(lse_np[0, h] - lse_ref.reshape(-1)) <= bound), "LSE"
+        assert np.all(np.abs(s_np[0, h] - s_ref) <= rel * np.abs(s_ref) + 1e-3), "S"
+        x = np.where(vis, s_np[0, h], -np.inf)
+        p_ref = np.exp(x - x.max(axis=1, keepdims=True))
+        p_ref /= p_ref.sum(axis=1, keepdims=True)
+        assert np.all(np.abs(p_np[0, h] - p_ref) <= rel * p_ref + 1e-6), "P"
+        assert np.all(p_np[0, h][~vis] == 0.0)
+
+
 def test_guard_bands_untouched():
     """Ragged N: nothing is written outside o and lse."""
     B, H, N, d = 3, 5, 1000, 64

@@ -3,7 +3,8 @@ forward library whose C ABI is ``include/fa_fwd.h``.
 
 The functions named like the C entry points (``fa_fwd_bf16``, ``fa_fwd_f16``,
 ``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_tile_shape``,
-``fa_strerror``, ``fa_build_info``) only marshal arguments: pointers are
+``fa_strerror``, ``fa_build_info``, and ``fa_standard_fwd`` of
+``include/fa_standard.h``, the materialising baseline) only marshal arguments: pointers are
 plain integers (device addresses), the stream an integer ``hipStream_t``
 handle, and the C status code is returned unchanged.
 
@@ -49,6 +50,7 @@ SIGNATURES = {
     "fa_fwd_tile_shape": (_I, [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_build_info": (ctypes.c_char_p, []),
+    "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
 }
 
 
@@ -106,6 +108,33 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
     a = FaArgs(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
                out_dtype, tile_q, tile_k, counters)
     return lib().fa_fwd_ex(ctypes.byref(a))
+
+
+def fa_standard_fwd(q, k, v, o, lse, s, p, B, H, N, d, scale, causal, stream, dtype):
+    return lib().fa_standard_fwd(q, k, v, o, lse, s, p, B, H, N, d, scale, causal, stream, dtype)
+
+
+def standard_attention(q, k, v, causal=False, scale=None):
+    """The standard (materialising) forward of include/fa_standard.h on the
+    device: returns ``(o, lse, s, p)`` with the N x N score and probability
+    matrices it wrote (16-bit inputs only)."""
+    import math
+    import torch
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, H, N, N), dtype=q.dtype, device=q.device)
+    p = torch.empty_like(s)
+    st = fa_standard_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), s.data_ptr(),
+                         p.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                         torch.cuda.current_stream(q.device).cuda_stream, dtype_code(q.dtype))
+    if st == FA_ERR_INVALID:
+        raise ValueError(f"fa_standard_fwd: {fa_strerror(st)}")
+    if st != FA_OK:
+        raise FaError(st, "fa_standard_fwd")
+    return o, lse, s, p
 
 
 def fa_fwd_tile_shape(dtype, d, causal):
