@@ -28,6 +28,10 @@ Modules:
   model).
 * ``memory``     -- the P2 memory-model helpers and the P1 §1.2 budget rows.
 * ``merge``      -- the P3 blocked-softmax merge on a vector.
+* ``backward``   -- ``attention_bwd_ref`` (dQ, dK, dV of the forward's
+  definition by the chain rule, P materialised; the gradients the P3
+  recomputation pillar rebuilds tile by tile) and ``brute_bwd_ref`` (scalar
+  loops); pinned by finite differences of ``attention_ref``.
 
 Every function here is pinned by tests against values the pages print, closed
 forms, invariants, a library routine, or brute force; none is "parity
@@ -40,6 +44,7 @@ from .memory import (score_bytes, tiles_1d, score_tiles, score_tile_bytes,
                      working_set_bytes, tile_tradeoff, materialization_ratio,
                      sram_budget, sram_formula_as_printed)
 from .merge import blocked_softmax
+from .backward import attention_bwd_ref, brute_bwd_ref
 
 __all__ = [
     "attention_ref", "attention_probs", "tiled_ref", "brute_ref",
@@ -47,4 +52,5 @@ __all__ = [
     "score_bytes", "tiles_1d", "score_tiles", "score_tile_bytes",
     "working_set_bytes", "tile_tradeoff", "materialization_ratio",
     "sram_budget", "sram_formula_as_printed", "blocked_softmax",
+    "attention_bwd_ref", "brute_bwd_ref",
 ]
