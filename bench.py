@@ -24,6 +24,10 @@ registers, spills, LDS bytes and occupancy beside the working set of
 "FlashAttention Memory Model" Q3 (Q, K, V, O and S tiles in 16 bits).
 --summarize l2 DIR reads a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run of it.
 
+--backward times only the backward pass (include/fa_bwd.h) on the same
+shape, non-causal and causal (after the copy kernel, for counter runs); the
+default line carries the same figures in its "backward" object.
+
 --standard times the standard forward of include/fa_standard.h (S and P
 materialised in HBM) on the same workload, after the copy kernel of
 --profile-run, so that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of it give
@@ -121,6 +125,66 @@ def time_workload(wl, causal, steps, warmup):
     del q, k, v, o, lse
     return dict(ms_per_step=bracket_ms / steps, launch_mean_ms=sum(per) / len(per),
                 launch_median_ms=per[len(per) // 2], launch_min_ms=per[0])
+
+
+def backward_flops(wl, causal):
+    """10 B H N^2 d: the five N x N x d products of the backward (recomputed
+    S, dP, dV, dK, dQ), 2.5 times the forward's convention, halved causal.
+    The kernels run seven (S and dP in each of the two kernels); the extra
+    work is not counted."""
+    return 2.5 * wl.flops(causal)
+
+
+def time_backward(wl, causal, steps, warmup):
+    """fa_bwd (dQ and D kernel, then dK/dV kernel) on a workload; the
+    forward runs once beforehand for O and LSE.  Returns ms per step."""
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    q, k, v = (upload(w, wl.dtype) for w in words)
+    do = upload(W.encode(W.draw_dout(wl.shape, W.default_seed()), wl.dtype), wl.dtype)
+    scale = W.scale_for(wl.d)
+    o, lse = fa.attention(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+    B, H, N, d = wl.shape
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, int(causal),
+            stream.cuda_stream, fa.dtype_code(q.dtype))
+
+    def step():
+        st = fa.fa_bwd(*args)
+        if st != fa.FA_OK:
+            raise RuntimeError(f"fa_bwd failed: {fa.fa_strerror(st)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del q, k, v, do, o, lse, dq, dk, dv, delta
+    return ms
+
+
+def backward_summary(steps, warmup):
+    import fa_workloads as W
+    out = {}
+    for key, name, causal in (("non_causal", "C2b", False), ("causal", "C3", True)):
+        wl = W.WORKLOADS[name]
+        ms = time_backward(wl, causal, steps, warmup)
+        tf = backward_flops(wl, causal) / (ms * 1e-3) / 1e12
+        out[key] = {"ms_per_step": round(ms, 5), "value": round(tf, 2), "frac": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    out["unit"] = "TFLOP/s"
+    out["workload"] = ("backward with recomputation (dQ, dK, dV from O, LSE, dO), B=4 H=16 N=4096 d=128 bf16; "
+                       "causal with 1% of key rows x8; 10 B H N^2 d FLOPs, halved causal")
+    return out
 
 
 def cpu_baseline(seconds):
@@ -382,6 +446,7 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="tile-size sweep table")
     ap.add_argument("--standard", action="store_true", help="time the standard (materialising) forward")
+    ap.add_argument("--backward", action="store_true", help="time only the backward pass (fa_bwd)")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
                          "'trace DIR [STEPS]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
@@ -410,6 +475,10 @@ def main():
     if a.standard:
         standard_baseline(a.steps, a.warmup)
         return
+    if a.backward:
+        copy_calibration()
+        print(json.dumps({"backward": backward_summary(a.steps, a.warmup)}), flush=True)
+        return
 
     wl = W.WORKLOADS["C2b"]
     r = time_workload(wl, False, a.steps, a.warmup)
@@ -422,6 +491,7 @@ def main():
     fc = wc.flops(True)
     causal_value = fc / (rc["ms_per_step"] * 1e-3) / 1e12
 
+    bwd = backward_summary(max(10, a.steps // 4), max(5, a.warmup // 4))
     traffic = traffic_for_kernel()
     out = {
         "metric": METRIC,
@@ -447,6 +517,7 @@ def main():
                    "value": round(causal_value, 2), "unit": "TFLOP/s",
                    "ms_per_step": round(rc["ms_per_step"], 5),
                    "frac": round(fc / (rc["launch_mean_ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)},
+        "backward": bwd,
         "launch_ms": {"mean": round(r["launch_mean_ms"], 5), "median": round(r["launch_median_ms"], 5),
                       "min": round(r["launch_min_ms"], 5)},
         "hbm_min_gbs": round((4 * wl.B * wl.H * wl.N * wl.d * 2 + 4 * wl.B * wl.H * wl.N)

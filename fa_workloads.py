@@ -15,6 +15,9 @@ Recipe (one per workload, seed 0 unless ``FA_SEED`` says otherwise):
   three tensors by 0.5 (standard deviation 0.5).
 * The 16-bit encodings round to nearest even: IEEE half via numpy, bfloat16
   by rounding the float32 bit pattern.
+* The backward's output gradient dO is a fourth tensor of float32 standard
+  normals from ``default_rng([seed, 1])`` (``draw_dout``), encoded the same
+  way.
 * ``scale`` is float32(1 / sqrt(d)), the value handed to the device; the
   oracle widens that same float32 to float64.
 
@@ -92,6 +95,13 @@ def draw_f32(shape, values="normal", seed=0):
     elif values != "normal":
         raise ValueError(f"unknown value recipe {values!r}")
     return q, k, v
+
+
+def draw_dout(shape, seed=0):
+    """The output gradient dO for the backward workloads: float32 standard
+    normals of ``shape`` from its own generator, ``default_rng([seed, 1])``,
+    so that the Q, K, V draws of the same seed are unchanged."""
+    return np.random.default_rng([seed, 1]).standard_normal(shape, dtype=np.float32)
 
 
 def bf16_encode(x):

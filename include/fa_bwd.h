@@ -1,0 +1,71 @@
+/*
+ * fa_bwd.h -- C ABI of the attention backward pass with recomputation.
+ *
+ * "Flash Attention 原理" names recomputation as the method's second pillar:
+ * the forward pass keeps each row's softmax statistics instead of the N x N
+ * probability matrix, and the backward pass rebuilds the probabilities tile
+ * by tile from them.  Here the kept statistic is the forward's per-row
+ * log-sum-exp (fa_fwd.h), so that for every head
+ *
+ *   P      = exp(scale * Q K^T - LSE)            (rebuilt per tile, never stored;
+ *                                                 0 where key > query when causal)
+ *   D[i]   = sum_c dO[i,c] O[i,c]                (= sum_j P[i,j] dP[i,j])
+ *   dV     = P^T dO
+ *   dP     = dO V^T
+ *   dS     = P * (dP - D)                        (row-wise softmax Jacobian)
+ *   dQ     = scale * dS K
+ *   dK     = scale * dS^T Q
+ *
+ * the gradients of the forward O = softmax(scale Q K^T [causal]) V of
+ * "FlashAttention分块计算优化Transformer显存效率" §1.1 and §2.2 at the output
+ * gradient dO.
+ *
+ * Entry points (one per element type, plus a generic form with a trailing
+ * dtype as in fa_fwd.h):
+ *
+ *   q, k, v, o, dout : device, const, dense row-major [B, H, N, d] of the
+ *                      element type; o and lse are the forward's outputs for
+ *                      the same q, k, v, scale and causal.
+ *   lse              : device, const, [B, H, N] fp32 (natural log).
+ *   dq, dk, dv       : device, written, [B, H, N] x d of the element type.
+ *   delta            : device, written, [B, H, N] fp32 work array (D above);
+ *                      the caller allocates it, the library allocates nothing.
+ *   B, H, N, d       : sizes; d = 64 or 128.
+ *   scale, causal    : as in the forward call.
+ *   stream           : hipStream_t as an opaque pointer; work is enqueued on
+ *                      it (two kernels: dQ and D first, then dK and dV) and
+ *                      the call returns without synchronising.
+ *
+ * Ownership: the caller owns every buffer.  The outputs and delta must not
+ * overlap any input or each other; the inputs may alias one another.
+ *
+ * Errors (fa_status of fa_fwd.h); every check runs before any HIP call:
+ * FA_ERR_INVALID for a null pointer, B, H, N or d <= 0, causal not 0 or 1, a
+ * non-finite scale, or an output overlapping an input or another output;
+ * FA_ERR_UNSUPPORTED for fp32 (no backward kernel is built for it), d other
+ * than 64 or 128, a head of 2^31 bytes or more, or a grid beyond 2^31
+ * workgroups; FA_ERR_HIP if a launch fails.  Faults inside a kernel surface
+ * at the caller's next synchronisation.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int fa_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+                void* stream);
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
+           int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

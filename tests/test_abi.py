@@ -156,3 +156,33 @@ def test_missing_library_fails_loudly(tmp_path):
 def test_struct_layout_matches_header():
     # 5 pointers, 4 ints, float, int, pointer, 4 ints, pointer on LP64
     assert ctypes.sizeof(fa.FaArgs) == 5 * 8 + 4 * 4 + 4 + 4 + 8 + 4 * 4 + 8
+
+
+def test_backward_argument_checks():
+    DO, DQ, DK, DV, DL = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+    def bwd(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, H=3, N=100, d=64,
+                 scale=0.125, causal=0, stream=None, dtype=fa.FA_DTYPE_BF16)
+        a.update(over)
+        return fa.fa_bwd(**a)
+    nbytes = 2 * 3 * 100 * 64 * 2
+    for field in ("B", "H", "N", "d"):
+        assert bwd(**{field: 0}) == fa.FA_ERR_INVALID
+        assert bwd(**{field: -3}) == fa.FA_ERR_INVALID
+    for field in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta"):
+        assert bwd(**{field: None}) == fa.FA_ERR_INVALID
+    assert bwd(causal=2) == fa.FA_ERR_INVALID
+    assert bwd(scale=float("inf")) == fa.FA_ERR_INVALID
+    assert bwd(dq=Q + nbytes - 2) == fa.FA_ERR_INVALID            # output over an input
+    assert bwd(dv=DK + 64) == fa.FA_ERR_INVALID                   # outputs overlap each other
+    assert bwd(delta=L + 4) == fa.FA_ERR_INVALID                  # work array over the lse input
+    assert bwd(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(dtype=9) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(N=1 << 23, d=128) == fa.FA_ERR_UNSUPPORTED
+    # inputs may alias each other; with valid arguments the call only fails for lack of a GPU
+    assert bwd(k=Q, v=Q) in (fa.FA_ERR_HIP, fa.FA_OK)
+    for fn in (fa.fa_bwd_bf16, fa.fa_bwd_f16):
+        assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 0, 1, 1, 64, 1.0, 0, None) == fa.FA_ERR_INVALID
+        assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 1, 1, 48, 1.0, 0, None) == fa.FA_ERR_UNSUPPORTED

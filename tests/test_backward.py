@@ -1,0 +1,149 @@
+"""GPU parity of the HIP backward pass (include/fa_bwd.h) against the float64
+backward oracle (oracle.backward).
+
+The device path is the composite the backward is built for: the HIP forward
+writes O and LSE, the HIP backward rebuilds P from that LSE
+("Flash Attention 原理", two pillars: recomputation) and returns dQ, dK, dV.
+The oracle computes the exact gradients from Q, K, V and dO alone; nothing it
+uses comes from the device.
+
+Gate.  No tolerance is stated for gradients, and gradients have no fixed
+scale, so the forward's output tolerances (1e-2 for bf16, 2e-3 for fp16,
+applied there to outputs of order one) are applied relative to the largest
+reference entry of each gradient:
+max(|g - g_ref| - half_ulp(g_ref)) <= tol * max|g_ref|, the half ulp being
+the rounding of the 16-bit output itself.  A CPU emulation of the kernels'
+arithmetic (P and dS rounded to the input type before their products, fp32
+sums, O rounded to 16 bits) gives at most 6.1e-3 (bf16) and 9.0e-4 (fp16) on
+the shapes below.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import oracle
+import tiled_exact_attention_fwd_amd as fa
+from parity_util import half_ulp, out_to64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f16": 2e-3}
+
+
+def inputs(shape, dtype, values, seed):
+    words = W.make_words(shape, dtype, values, seed)
+    dwords = W.encode(W.draw_dout(shape, seed), dtype)
+    return words, dwords
+
+
+def run_device(words, dwords, dtype, causal, scale):
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    dod = to_dev(dwords, dtype)
+    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (qd, kd, vd, dod, o, lse), (dq, dk, dv, delta)
+
+
+def grad_errors(dev, ref, dtype):
+    out = {}
+    for name, g, r in zip(("dq", "dk", "dv"), dev, ref):
+        scale = float(np.max(np.abs(r))) or 1.0
+        ex = float(np.max(np.abs(g - r) - half_ulp(np.maximum(np.abs(r), np.abs(g)), dtype))) if r.size else 0.0
+        out[name] = ex / scale
+    return out
+
+
+def check(words, dwords, dtype, causal, scale, heads=None, what=""):
+    B, H, N, d = words[0].shape
+    _, (dq, dk, dv, delta) = run_device(words, dwords, dtype, causal, scale)
+    g = [out_to64(t) for t in (dq, dk, dv)]
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    vals = [np.stack([W.decode64(w[b, h], dtype) for b, h in heads])[:, None] for w in (*words, dwords)]
+    ref = oracle.attention_bwd_ref(*vals, scale, causal)
+    dev = [np.stack([t[b, h] for b, h in heads])[:, None] for t in g]
+    errs = grad_errors(dev, ref, dtype)
+    for name, e in errs.items():
+        assert e <= TOL[dtype], f"{what} {dtype} causal={causal} N={N} d={d}: {errs}"
+    for t in g:
+        assert np.all(np.isfinite(t))
+    return errs, (dq, dk, dv, delta)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 200, 257])
+def test_small(dtype, d, causal, N):
+    print(f"backward small {dtype} d={d} causal={causal} N={N}", flush=True)
+    words, dwords = inputs((1, 2, N, d), dtype, "normal", 3)
+    errs, _ = check(words, dwords, dtype, causal, W.scale_for(d), what="small")
+    print(errs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_spiky_causal(dtype):
+    print(f"backward spiky {dtype}", flush=True)
+    words, dwords = inputs((2, 2, 640, 128), dtype, "spiky", 5)
+    errs, _ = check(words, dwords, dtype, True, W.scale_for(128), what="spiky")
+    print(errs)
+
+
+@pytest.mark.parametrize("name,causal", [("C2b", False), ("C3", True), ("C4", True), ("C4", False)])
+def test_workload_shapes(name, causal):
+    """The forward workloads' full shapes; the oracle checks a few whole
+    heads, and every head must satisfy sum_k dK[k] = 0 (softmax ignores a
+    shift shared by all keys)."""
+    wl = W.WORKLOADS[name]
+    print(f"backward workload {name} causal={causal} shape={wl.shape}", flush=True)
+    words, dwords = inputs(wl.shape, wl.dtype, wl.values, W.default_seed())
+    B, H, N, d = wl.shape
+    allh = [(b, h) for b in range(B) for h in range(H)]
+    heads = [allh[0], allh[len(allh) // 2], allh[-1]]
+    errs, (dq, dk, dv, delta) = check(words, dwords, wl.dtype, causal, W.scale_for(d), heads=heads, what=name)
+    print(name, causal, errs)
+    colsum = dk.float().sum(dim=2).abs().max().item()
+    dkmax = dk.float().abs().max().item()
+    # the sum of N rounded terms: each carries the gate's relative error at most
+    assert colsum <= TOL[wl.dtype] * dkmax * N ** 0.5, (colsum, dkmax)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_closed_forms_and_determinism(dtype):
+    # N = 1: O = V whatever the scores, so dQ = dK = 0 and dV = dO.  On the
+    # device P = exp(s - LSE) is 1 within fp32 rounding and rounds to exactly 1
+    # for the dV product; dS = P (dP - D) is the difference of two fp32 dot
+    # products of the same 64 terms summed in different orders, so dQ and dK
+    # are zero up to that rounding.
+    words, dwords = inputs((2, 3, 1, 64), dtype, "normal", 7)
+    (qd, kd, vd, dod, _, _), (dq, dk, dv, _) = run_device(words, dwords, dtype, False, W.scale_for(64))
+    bound = 64 * 2.0 ** -22 * float((dod.float().abs() * vd.float().abs()).sum(dim=3).max())
+    bound *= float(max(qd.float().abs().max(), kd.float().abs().max()))
+    assert float(dq.float().abs().max()) <= bound and float(dk.float().abs().max()) <= bound
+    assert torch.equal(dv.view(torch.int16), dod.view(torch.int16))
+    # repeated launches give the same bits
+    words, dwords = inputs((2, 2, 300, 128), dtype, "normal", 8)
+    for causal in (False, True):
+        _, a = run_device(words, dwords, dtype, causal, W.scale_for(128))
+        _, b = run_device(words, dwords, dtype, causal, W.scale_for(128))
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x.view(torch.int16),
+                               y.view(torch.int32) if y.dtype == torch.float32 else y.view(torch.int16))
+
+
+def test_entry_points_agree():
+    words, dwords = inputs((1, 2, 130, 64), "bf16", "normal", 9)
+    (qd, kd, vd, dod, o, lse), (dq, dk, dv, delta) = run_device(words, dwords, "bf16", True, 0.125)
+    outs = [torch.empty_like(t) for t in (dq, dk, dv, delta)]
+    st = fa.fa_bwd_bf16(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), dod.data_ptr(),
+                        *[t.data_ptr() for t in outs], 1, 2, 130, 64, 0.125, 1,
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    for x, y in zip(outs, (dq, dk, dv, delta)):
+        assert torch.equal(x, y)
+    # the work array holds rowsum(dO * O) of the forward's stored O
+    ref = (dod.float() * o.float()).sum(dim=3)
+    assert torch.allclose(delta, ref, atol=1e-4, rtol=1e-5)

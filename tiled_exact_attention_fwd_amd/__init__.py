@@ -3,8 +3,10 @@ forward library whose C ABI is ``include/fa_fwd.h``.
 
 The functions named like the C entry points (``fa_fwd_bf16``, ``fa_fwd_f16``,
 ``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_tile_shape``,
-``fa_strerror``, ``fa_build_info``, and ``fa_standard_fwd`` of
-``include/fa_standard.h``, the materialising baseline) only marshal arguments: pointers are
+``fa_strerror``, ``fa_build_info``, ``fa_standard_fwd`` of
+``include/fa_standard.h``, the materialising baseline, and ``fa_bwd_bf16``,
+``fa_bwd_f16``, ``fa_bwd`` of ``include/fa_bwd.h``, the backward with
+recomputation) only marshal arguments: pointers are
 plain integers (device addresses), the stream an integer ``hipStream_t``
 handle, and the C status code is returned unchanged.
 
@@ -30,6 +32,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _FWD12 = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]
+_BWD17 = [_P] * 10 + [_I, _I, _I, _I, _F, _I, _P]
 
 
 class FaArgs(ctypes.Structure):
@@ -51,6 +54,9 @@ SIGNATURES = {
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_build_info": (ctypes.c_char_p, []),
     "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
+    "fa_bwd_bf16": (_I, _BWD17),
+    "fa_bwd_f16": (_I, _BWD17),
+    "fa_bwd": (_I, _BWD17 + [_I]),
 }
 
 
@@ -135,6 +141,53 @@ def standard_attention(q, k, v, causal=False, scale=None):
     if st != FA_OK:
         raise FaError(st, "fa_standard_fwd")
     return o, lse, s, p
+
+
+def fa_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream):
+    return lib().fa_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+
+
+def fa_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream):
+    return lib().fa_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype):
+    return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype)
+
+
+def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of the attention forward on the device
+    (include/fa_bwd.h), from the forward's ``o`` and ``lse`` for the same
+    inputs and the output gradient ``dout`` (16-bit [B, H, N, d] tensors,
+    lse [B, H, N] fp32).  Also returns the ``delta`` work array the call
+    wrote (rowsum(dout * o), fp32)."""
+    import math
+    import torch
+    ts = (q, k, v, o, dout)
+    if not all(t.dtype == q.dtype for t in ts):
+        raise ValueError("q, k, v, o, dout must share one dtype")
+    if q.dim() != 4 or not all(t.shape == q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must all be [B, H, N, d]")
+    for t in ts + (lse,):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("inputs must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be fp32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
+                int(bool(causal)), stream, dtype_code(q.dtype))
+    if st == FA_ERR_INVALID:
+        raise ValueError(f"fa_bwd: {fa_strerror(st)}")
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv, delta
 
 
 def fa_fwd_tile_shape(dtype, d, causal):

@@ -5,8 +5,9 @@
 The library is plain C ABI (include/fa_fwd.h); the Python binding loads it
 with ctypes.  The kernel instances live in separate translation units
 (fa_fwd_inst16.hip once per element type, head dimension and mask;
-fa_fwd_inst32.hip once per mask) that compile in parallel and are linked
-with the host layer (fa_fwd.hip).  Packed-fp32 VALU instructions are
+fa_fwd_inst32.hip once per mask; fa_bwd_inst.hip, the backward, once per
+element type and head dimension) that compile in parallel and are linked
+with the host layers (fa_fwd.hip, fa_standard.hip, fa_bwd.hip).  Packed-fp32 VALU instructions are
 disabled: hipcc would otherwise form them from ordinary float code.
 """
 
@@ -38,6 +39,11 @@ for t in ("bf16", "f16"):
                           [f"-DFA_INST_T={t}", f"-DFA_INST_D={d}", f"-DFA_INST_C={c}"]))
 for c in (0, 1):
     UNITS.append((f"inst32_c{c}", "fa_fwd_inst32.hip", [f"-DFA_INST_C={c}"]))
+# backward kernels, one unit per element type and head dimension
+UNITS.append(("fa_bwd", "fa_bwd.hip", []))
+for t in ("bf16", "f16"):
+    for d in (64, 128):
+        UNITS.append((f"bwd_{t}_d{d}", "fa_bwd_inst.hip", [f"-DFA_INST_T={t}", f"-DFA_INST_D={d}"]))
 # tile-size sweep shapes (bf16, d = 128, no mask)
 for tq in (64, 128, 256):
     for tk in (32, 64, 128):

@@ -1,0 +1,86 @@
+// Host layer of the attention backward (include/fa_bwd.h): argument checks,
+// then the two kernels of fa_bwd_kernels.h on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_bwd.h"
+#include "fa_bwd_kernels.h"
+#include "fa_bwd_launch.h"
+#include "fa_fwd.h"
+
+namespace {
+
+bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int run(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+        void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
+        int dtype) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID;
+    if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((uint64_t)N * d * 2 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    const uint64_t heads = (uint64_t)B * H, nblk = ((uint64_t)N + 127) / 128;
+    if (heads * nblk >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    const uint64_t tb = heads * N * d * 2, sb = heads * N * 4;
+    const void* ins[6] = {q, k, v, o, dout, lse};
+    const uint64_t inb[6] = {tb, tb, tb, tb, tb, sb};
+    void* outs[4] = {dq, dk, dv, delta};
+    const uint64_t outb[4] = {tb, tb, tb, sb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], outb[i], ins[j], inb[j])) return FA_ERR_INVALID;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outb[i], outs[j], outb[j])) return FA_ERR_INVALID;
+    }
+    fa::bwd::BwdParams p;
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o; p.dout = (const uint16_t*)dout; p.lse = lse;
+    p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv; p.delta = delta;
+    p.N = N;
+    p.nblk = (int)nblk;
+    p.c = scale * fa::bwd::kLog2e;
+    p.scale = scale;
+    const bool c = causal != 0;
+    int rc;
+    if (dtype == FA_DTYPE_BF16)
+        rc = d == 64 ? fa::bwd::launch_bwd_bf16_d64(p, (int)heads, c, stream)
+                     : fa::bwd::launch_bwd_bf16_d128(p, (int)heads, c, stream);
+    else
+        rc = d == 64 ? fa::bwd::launch_bwd_f16_d64(p, (int)heads, c, stream)
+                     : fa::bwd::launch_bwd_f16_d128(p, (int)heads, c, stream);
+    return rc == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
+           int dtype) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype);
+}
+
+int fa_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+                void* stream) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, FA_DTYPE_BF16);
+}
+
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, FA_DTYPE_F16);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Backward kernel instances of one element type and head dimension
+// (FA_INST_T, FA_INST_D), both mask settings, and their launcher.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_bwd_kernels.h"
+#include "fa_bwd_launch.h"
+
+#if !defined(FA_INST_T) || !defined(FA_INST_D)
+#error "FA_INST_T and FA_INST_D select the instance"
+#endif
+
+#define FA_CAT4(a, b, c, d) a##b##c##d
+#define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
+#define FA_NAME FA_XCAT4(launch_bwd_, FA_INST_T, _d, FA_INST_D)
+
+namespace fa {
+namespace bwd {
+
+namespace {
+struct bf16 { using T = BF16; };
+struct f16 { using T = F16; };
+
+template <class T, int D, bool C>
+int launch(const BwdParams& p, int heads, void* stream) {
+    const dim3 grid((unsigned)(heads * p.nblk)), block(256);
+    const hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL((dq_kernel<T, D, C>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<T, D, C>), grid, block, 0, st, p);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+}  // namespace
+
+int FA_NAME(const BwdParams& p, int heads, bool causal, void* stream) {
+    using T = FA_INST_T::T;
+    return causal ? launch<T, FA_INST_D, true>(p, heads, stream) : launch<T, FA_INST_D, false>(p, heads, stream);
+}
+
+}  // namespace bwd
+}  // namespace fa

@@ -1,0 +1,312 @@
+// Attention backward kernels for gfx950 (CDNA4, wave64, MFMA), with the
+// probabilities recomputed tile by tile from the forward's log-sum-exp
+// ("Flash Attention 原理", two pillars: recomputation).  The gradients are
+// those of the forward of "FlashAttention分块计算优化Transformer显存效率"
+// §1.1 / §2.2, O = softmax(scale Q K^T [causal]) V:
+//
+//   P = exp2(c s - LSE log2 e) with c = scale log2 e    (0 where masked)
+//   D = rowsum(dO * O),  dS = P * (dO V^T - D)
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+//
+// Two kernels, launched in this order on one stream:
+//
+//   dq_kernel    one workgroup = 128 query rows of one head (4 waves x 32
+//                rows); the wave's Q and dO rows stay in registers, K and V
+//                tiles of 64 keys pass through LDS.  Per 32-key block it
+//                computes S^T = K Q^T and dP^T = V dO^T (a lane holds one
+//                query), dS^T, and dQ^T += K^T dS^T; it also computes D for
+//                its rows from O and dO and writes it for the second kernel.
+//   dkdv_kernel  one workgroup = 128 keys of one head (4 waves x 32 keys);
+//                the wave's K and V rows stay in registers, Q and dO tiles of
+//                64 queries (with their LSE and D) pass through LDS.  Per
+//                32-query block it computes S = Q K^T and dP = dO V^T (a lane
+//                holds one key), dS, and dV^T += dO^T P, dK^T += Q^T dS.
+//
+// Each kernel recomputes S and dP for the pairs it visits, so the backward
+// runs seven N x N x d products per head where one that stored partial dQ
+// sums would run five; in exchange neither kernel needs atomics or a
+// reduction buffer and the results are deterministic.
+//
+// MFMA layout (v_mfma_f32_32x32x16_{bf16,f16}, C = A B): lane (li, lh) of
+// the wave (li = lane % 32, lh = lane / 32) supplies A[li][8 lh .. 8 lh + 7]
+// and B[8 lh .. 8 lh + 7][li] of each 16-deep step, and holds
+// C[8 (r / 4) + 4 lh + r % 4][li] in accumulator register r.  The product of
+// a 32-row block of S (or S^T) with a third matrix takes registers 8t..8t+7
+// of the first result as the B operand of step t: its k index e then stands
+// for row 16 t + 4 lh + 8 (e / 4) + e % 4, and the A operand is read with
+// the same index order from a row-major tile in LDS by the transposing read
+// ds_read_b64_tr_b16 (each 16-lane group hands lane s four consecutive rows
+// of column s of a 4 x 16 block whose row s / 4, columns 4 (s % 4) .. +3 it
+// addressed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_fwd_kernels.h"
+
+namespace fa {
+namespace bwd {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float* lse;
+    uint16_t *dq, *dk, *dv;
+    float* delta;
+    int N;
+    int nblk;      // 128-row blocks per head
+    float c;       // scale * log2(e)
+    float scale;
+};
+
+template <class T> __device__ __forceinline__ float to_f32(uint32_t h);
+template <> __device__ __forceinline__ float to_f32<BF16>(uint32_t h) { return __uint_as_float(h << 16); }
+template <> __device__ __forceinline__ float to_f32<F16>(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// dot product of two 8-element 16-bit vectors in fp32
+template <class T> __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s += to_f32<T>(a[i] & 0xffffu) * to_f32<T>(b[i] & 0xffffu);
+        s += to_f32<T>(a[i] >> 16) * to_f32<T>(b[i] >> 16);
+    }
+    return s;
+}
+
+template <int D>
+struct Geo {
+    static constexpr int NS = D / 16;          // 16-deep steps over the head dimension
+    static constexpr int NDB = D / 32;         // 32-column blocks of the head dimension
+    static constexpr int PITCH = D * 2 + 16;   // LDS row pitch in bytes (padded against bank conflicts)
+    static constexpr int TILE = 64;            // rows per LDS tile
+    static constexpr int CHUNKS = TILE * D / 8;  // 16-byte pieces per tile
+};
+
+// Copies rows [r0, r0 + 64) of one head (row-major, D columns, 16-bit) into
+// an LDS tile with row pitch Geo<D>::PITCH; rows past the head's end read as
+// zeros through the buffer resource's extent.
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int r0, int tid) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int i = tid; i < G::CHUNKS; i += 256) {
+        const int row = i / (D / 8), ch = i % (D / 8);
+        const u32x4_t x = buf_load16(r, (uint32_t)(((r0 + row) * D + ch * 8) * 2));
+        *(u32x4_t*)(lds + row * G::PITCH + ch * 16) = x;
+    }
+}
+
+// A operand of step t taken from a row-major LDS tile: rows blk + 16 t + 4 lh
+// + 8 (e / 4) + e % 4 (e = 0..7), column col0 + li (col0 a multiple of 32).
+template <int D>
+__device__ __forceinline__ u32x4_t tr_operand(const uint8_t* lds, int blk, int t, int col0, int lane) {
+    using G = Geo<D>;
+    const int s = lane & 15, grp = lane >> 4, lh = lane >> 5;
+    const uint8_t* p = lds + (blk + 16 * t + 4 * lh + (s >> 2)) * G::PITCH + (col0 + 16 * (grp & 1) + 4 * (s & 3)) * 2;
+    const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 8 * G::PITCH);
+    return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// 16 fp32 results -> the two B operands (registers 8t .. 8t + 7 each)
+template <class T>
+__device__ __forceinline__ void pack_b(const float* x, u32x4_t* b) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        b[t] = u32x4_t{pack2<T>(x[8 * t + 0], x[8 * t + 1]), pack2<T>(x[8 * t + 2], x[8 * t + 3]),
+                       pack2<T>(x[8 * t + 4], x[8 * t + 5]), pack2<T>(x[8 * t + 6], x[8 * t + 7])};
+}
+
+// Stores a 32 x D transposed accumulator (acc[db] register r = column
+// 32 db + 8 (r / 4) + 4 lh + r % 4 of row `row`) times `mul` as 16-bit.
+template <class T, int D>
+__device__ __forceinline__ void store_rows(uint16_t* out, int row, int N, const f32x16_t* acc, float mul, int lh) {
+    if (row >= N) return;
+    uint16_t* p = out + (size_t)row * D + 4 * lh;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2_t w{pack2<T>(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                            pack2<T>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+            *(__attribute__((address_space(1))) u32x2_t*)(p + 32 * db + 8 * g) = w;
+        }
+}
+
+template <class T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
+    using G = Geo<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t ks[G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t vs[G::TILE * G::PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int N = p.N;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int hh = L / p.nblk;
+    int qb = L - hh * p.nblk;
+    if (CAUSAL) qb = p.nblk - 1 - qb;          // longest rows first
+    const int q0 = qb * 128, qw = q0 + 32 * wave, q = qw + li;
+    const size_t head = (size_t)hh * N * D;
+    const uint32_t hb = (uint32_t)N * D * 2;
+    const auto rq = make_rsrc(p.q + head, hb), rk = make_rsrc(p.k + head, hb), rv = make_rsrc(p.v + head, hb);
+    const auto ro = make_rsrc(p.o + head, hb), rdo = make_rsrc(p.dout + head, hb);
+
+    // the wave's rows as B operands: lane (li, lh) holds row q, columns 16 s + 8 lh .. +7
+    u32x4_t qreg[G::NS], dreg[G::NS];
+    float dsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s) {
+        const uint32_t off = (uint32_t)((q * D + 16 * s + 8 * lh) * 2);
+        qreg[s] = buf_load16(rq, off);
+        dreg[s] = buf_load16(rdo, off);
+        dsum += dot8<T>(dreg[s], buf_load16(ro, off));
+    }
+    dsum = sum_halves(dsum);
+    const bool qok = q < N;
+    if (qok && lh == 0) p.delta[(size_t)hh * N + q] = dsum;
+    const float lse2 = qok ? p.lse[(size_t)hh * N + q] * kLog2e : __builtin_inff();
+    const float c = p.c;
+
+    f32x16_t acc[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16_t{};
+
+    const int kend = CAUSAL ? min(N, q0 + 128) : N;
+    const int nkt = (kend + G::TILE - 1) / G::TILE;
+    for (int kt = 0; kt < nkt; ++kt) {
+        __syncthreads();
+        load_tile<D>(rk, ks, kt * G::TILE, tid);
+        load_tile<D>(rv, vs, kt * G::TILE, tid);
+        __syncthreads();
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int k0 = kt * G::TILE + 32 * sub;
+            if (k0 >= N || (CAUSAL && k0 > qw + 31)) continue;   // wave-uniform: no visible key
+            // S^T and dP^T: A = K / V rows (key k0 + li), B = this wave's Q / dO rows
+            f32x16_t st{}, dpt{};
+#pragma unroll
+            for (int s = 0; s < G::NS; ++s) {
+                const int off = (32 * sub + li) * G::PITCH + (16 * s + 8 * lh) * 2;
+                st = mma<T>(*(const u32x4_t*)(ks + off), qreg[s], st);
+                dpt = mma<T>(*(const u32x4_t*)(vs + off), dreg[s], dpt);
+            }
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r / 4) + 4 * lh + (r % 4);
+                const bool vis = key < N && (!CAUSAL || key <= q);
+                const float pr = vis ? exp2f(c * st[r] - lse2) : 0.f;
+                ds[r] = pr * (dpt[r] - dsum);
+            }
+            u32x4_t b[2];
+            pack_b<T>(ds, b);
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+                    acc[db] = mma<T>(tr_operand<D>(ks, 32 * sub, t, 32 * db, lane), b[t], acc[db]);
+        }
+    }
+    store_rows<T, D>(p.dq + head, q, N, acc, p.scale, lh);
+}
+
+template <class T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
+    using G = Geo<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t qs[G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t dos[G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) float lses[G::TILE];
+    __shared__ __attribute__((aligned(16))) float dls[G::TILE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int N = p.N;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int hh = L / p.nblk;
+    const int kb = L - hh * p.nblk;            // causal: block 0 sees the most queries
+    const int k0 = kb * 128, kw = k0 + 32 * wave, key = kw + li;
+    const size_t head = (size_t)hh * N * D;
+    const uint32_t hb = (uint32_t)N * D * 2;
+    const auto rq = make_rsrc(p.q + head, hb), rk = make_rsrc(p.k + head, hb), rv = make_rsrc(p.v + head, hb);
+    const auto rdo = make_rsrc(p.dout + head, hb);
+    const float* lse = p.lse + (size_t)hh * N;
+    const float* delta = p.delta + (size_t)hh * N;
+
+    // the wave's keys as B operands: lane (li, lh) holds row `key`, columns 16 s + 8 lh .. +7
+    u32x4_t kreg[G::NS], vreg[G::NS];
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s) {
+        const uint32_t off = (uint32_t)((key * D + 16 * s + 8 * lh) * 2);
+        kreg[s] = buf_load16(rk, off);
+        vreg[s] = buf_load16(rv, off);
+    }
+    const float c = p.c;
+
+    f32x16_t acck[G::NDB], accv[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        acck[db] = f32x16_t{};
+        accv[db] = f32x16_t{};
+    }
+
+    const int nqt = (N + G::TILE - 1) / G::TILE;
+    const int qt0 = CAUSAL ? k0 / G::TILE : 0;
+    for (int qt = qt0; qt < nqt; ++qt) {
+        __syncthreads();
+        load_tile<D>(rq, qs, qt * G::TILE, tid);
+        load_tile<D>(rdo, dos, qt * G::TILE, tid);
+        if (tid < G::TILE) {
+            const int r = qt * G::TILE + tid;
+            lses[tid] = r < N ? lse[r] * kLog2e : __builtin_inff();   // rows past N: P = 0
+            dls[tid] = r < N ? delta[r] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int qs0 = qt * G::TILE + 32 * sub;
+            if (qs0 >= N || (CAUSAL && qs0 + 31 < kw)) continue;   // wave-uniform: every query before every key
+            // S and dP: A = Q / dO rows (query qs0 + li), B = this wave's K / V rows
+            f32x16_t st{}, dpt{};
+#pragma unroll
+            for (int s = 0; s < G::NS; ++s) {
+                const int off = (32 * sub + li) * G::PITCH + (16 * s + 8 * lh) * 2;
+                st = mma<T>(*(const u32x4_t*)(qs + off), kreg[s], st);
+                dpt = mma<T>(*(const u32x4_t*)(dos + off), vreg[s], dpt);
+            }
+            float pr[16], ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int rl = 32 * sub + 8 * g + 4 * lh;          // local row of registers 4g .. 4g + 3
+                const f32x4_t l4 = *(const f32x4_t*)(lses + rl);
+                const f32x4_t d4 = *(const f32x4_t*)(dls + rl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e, qi = qs0 + 8 * g + 4 * lh + e;
+                    const bool vis = !CAUSAL || key <= qi;
+                    pr[r] = vis ? exp2f(c * st[r] - l4[e]) : 0.f;
+                    ds[r] = pr[r] * (dpt[r] - d4[e]);
+                }
+            }
+            u32x4_t bp[2], bd[2];
+            pack_b<T>(pr, bp);
+            pack_b<T>(ds, bd);
+            // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db) {
+                    accv[db] = mma<T>(tr_operand<D>(dos, 32 * sub, t, 32 * db, lane), bp[t], accv[db]);
+                    acck[db] = mma<T>(tr_operand<D>(qs, 32 * sub, t, 32 * db, lane), bd[t], acck[db]);
+                }
+        }
+    }
+    store_rows<T, D>(p.dk + head, key, N, acck, p.scale, lh);
+    store_rows<T, D>(p.dv + head, key, N, accv, 1.0f, lh);
+}
+
+}  // namespace bwd
+}  // namespace fa

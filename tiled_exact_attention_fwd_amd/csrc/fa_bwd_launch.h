@@ -1,0 +1,16 @@
+// Launchers of the backward kernel instances (one translation unit per
+// element type and head dimension); each returns 0, or -1 if a launch failed.
+#pragma once
+
+namespace fa {
+namespace bwd {
+
+struct BwdParams;
+
+int launch_bwd_bf16_d64(const BwdParams& p, int heads, bool causal, void* stream);
+int launch_bwd_bf16_d128(const BwdParams& p, int heads, bool causal, void* stream);
+int launch_bwd_f16_d64(const BwdParams& p, int heads, bool causal, void* stream);
+int launch_bwd_f16_d128(const BwdParams& p, int heads, bool causal, void* stream);
+
+}  // namespace bwd
+}  // namespace fa
