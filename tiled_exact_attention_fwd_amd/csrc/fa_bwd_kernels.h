@@ -87,19 +87,30 @@ struct Geo {
     static constexpr int CHUNKS = TILE * D / 8;  // 16-byte pieces per tile
 };
 
-// Copies rows [r0, r0 + 64) of one head (row-major, D columns, 16-bit) into
-// an LDS tile with row pitch Geo<D>::PITCH; rows past the head's end read as
-// zeros through the buffer resource's extent.
+// A tile is rows [r0, r0 + 64) of one head (row-major, D columns, 16-bit),
+// copied HBM -> registers -> LDS (row pitch Geo<D>::PITCH): the loads of the
+// next tile are issued before the current tile is computed and stored to the
+// other LDS buffer after it, so their latency is hidden.  Rows past the head's end read as zeros through the buffer
+// resource's extent.
 template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int r0, int tid) {
-    using G = Geo<D>;
+struct TileRegs {
+    static constexpr int PER = Geo<D>::CHUNKS / 256;   // 16-byte pieces per thread
+    u32x4_t x[PER];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int r0, int tid) {
 #pragma unroll
-    for (int i = tid; i < G::CHUNKS; i += 256) {
-        const int row = i / (D / 8), ch = i % (D / 8);
-        const u32x4_t x = buf_load16(r, (uint32_t)(((r0 + row) * D + ch * 8) * 2));
-        *(u32x4_t*)(lds + row * G::PITCH + ch * 16) = x;
+        for (int u = 0; u < PER; ++u) {
+            const int i = tid + 256 * u, row = i / (D / 8), ch = i % (D / 8);
+            x[u] = buf_load16(r, (uint32_t)(((r0 + row) * D + ch * 8) * 2));
+        }
     }
-}
+    __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int i = tid + 256 * u, row = i / (D / 8), ch = i % (D / 8);
+            *(u32x4_t*)(lds + row * Geo<D>::PITCH + ch * 16) = x[u];
+        }
+    }
+};
 
 // A operand of step t taken from a row-major LDS tile: rows blk + 16 t + 4 lh
 // + 8 (e / 4) + e % 4 (e = 0..7), column col0 + li (col0 a multiple of 32).
@@ -140,8 +151,9 @@ __device__ __forceinline__ void store_rows(uint16_t* out, int row, int N, const 
 template <class T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t ks[G::TILE * G::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t vs[G::TILE * G::PITCH];
+    // K and V tiles, double-buffered
+    __shared__ __attribute__((aligned(16))) uint8_t ks[2][G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t vs[2][G::TILE * G::PITCH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const int N = p.N;
@@ -177,11 +189,21 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
 
     const int kend = CAUSAL ? min(N, q0 + 128) : N;
     const int nkt = (kend + G::TILE - 1) / G::TILE;
+    TileRegs<D> kr, vr;
+    kr.load(rk, 0, tid);
+    vr.load(rv, 0, tid);
+    kr.store(ks[0], tid);
+    vr.store(vs[0], tid);
+    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-        __syncthreads();
-        load_tile<D>(rk, ks, kt * G::TILE, tid);
-        load_tile<D>(rv, vs, kt * G::TILE, tid);
-        __syncthreads();
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nkt;
+        if (more) {                            // next tile in flight during this one
+            kr.load(rk, (kt + 1) * G::TILE, tid);
+            vr.load(rv, (kt + 1) * G::TILE, tid);
+        }
+        const uint8_t* kc = ks[cur];
+        const uint8_t* vc = vs[cur];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int k0 = kt * G::TILE + 32 * sub;
@@ -191,15 +213,15 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
 #pragma unroll
             for (int s = 0; s < G::NS; ++s) {
                 const int off = (32 * sub + li) * G::PITCH + (16 * s + 8 * lh) * 2;
-                st = mma<T>(*(const u32x4_t*)(ks + off), qreg[s], st);
-                dpt = mma<T>(*(const u32x4_t*)(vs + off), dreg[s], dpt);
+                st = mma<T>(*(const u32x4_t*)(kc + off), qreg[s], st);
+                dpt = mma<T>(*(const u32x4_t*)(vc + off), dreg[s], dpt);
             }
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = k0 + 8 * (r / 4) + 4 * lh + (r % 4);
                 const bool vis = key < N && (!CAUSAL || key <= q);
-                const float pr = vis ? exp2f(c * st[r] - lse2) : 0.f;
+                const float pr = vis ? __builtin_amdgcn_exp2f(c * st[r] - lse2) : 0.f;
                 ds[r] = pr * (dpt[r] - dsum);
             }
             u32x4_t b[2];
@@ -209,8 +231,14 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < G::NDB; ++db)
-                    acc[db] = mma<T>(tr_operand<D>(ks, 32 * sub, t, 32 * db, lane), b[t], acc[db]);
+                    acc[db] = mma<T>(tr_operand<D>(kc, 32 * sub, t, 32 * db, lane), b[t], acc[db]);
         }
+        // the other buffers were last read before the previous barrier
+        if (more) {
+            kr.store(ks[cur ^ 1], tid);
+            vr.store(vs[cur ^ 1], tid);
+        }
+        __syncthreads();
     }
     store_rows<T, D>(p.dq + head, q, N, acc, p.scale, lh);
 }
@@ -218,10 +246,11 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
 template <class T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t qs[G::TILE * G::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t dos[G::TILE * G::PITCH];
-    __shared__ __attribute__((aligned(16))) float lses[G::TILE];
-    __shared__ __attribute__((aligned(16))) float dls[G::TILE];
+    // Q and dO tiles with their rows' LSE (base 2) and D, double-buffered
+    __shared__ __attribute__((aligned(16))) uint8_t qs[2][G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t dos[2][G::TILE * G::PITCH];
+    __shared__ __attribute__((aligned(16))) float lses[2][G::TILE];
+    __shared__ __attribute__((aligned(16))) float dls[2][G::TILE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const int N = p.N;
@@ -255,16 +284,41 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
 
     const int nqt = (N + G::TILE - 1) / G::TILE;
     const int qt0 = CAUSAL ? k0 / G::TILE : 0;
-    for (int qt = qt0; qt < nqt; ++qt) {
-        __syncthreads();
-        load_tile<D>(rq, qs, qt * G::TILE, tid);
-        load_tile<D>(rdo, dos, qt * G::TILE, tid);
+    TileRegs<D> qr, dr;
+    float lpre = 0.f, dpre = 0.f;
+    // statistics of row r of tile qt: rows past N get LSE +inf, so P = 0 there
+    auto load_stats = [&](int qt) {
         if (tid < G::TILE) {
             const int r = qt * G::TILE + tid;
-            lses[tid] = r < N ? lse[r] * kLog2e : __builtin_inff();   // rows past N: P = 0
-            dls[tid] = r < N ? delta[r] : 0.f;
+            lpre = r < N ? lse[r] * kLog2e : __builtin_inff();
+            dpre = r < N ? delta[r] : 0.f;
         }
-        __syncthreads();
+    };
+    auto store_stats = [&](int b) {
+        if (tid < G::TILE) {
+            lses[b][tid] = lpre;
+            dls[b][tid] = dpre;
+        }
+    };
+    if (qt0 < nqt) {
+        qr.load(rq, qt0 * G::TILE, tid);
+        dr.load(rdo, qt0 * G::TILE, tid);
+        load_stats(qt0);
+        qr.store(qs[0], tid);
+        dr.store(dos[0], tid);
+        store_stats(0);
+    }
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int cur = (qt - qt0) & 1;
+        const bool more = qt + 1 < nqt;
+        if (more) {                            // next tile in flight during this one
+            qr.load(rq, (qt + 1) * G::TILE, tid);
+            dr.load(rdo, (qt + 1) * G::TILE, tid);
+            load_stats(qt + 1);
+        }
+        const uint8_t* qc = qs[cur];
+        const uint8_t* dc = dos[cur];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int qs0 = qt * G::TILE + 32 * sub;
@@ -274,20 +328,20 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int s = 0; s < G::NS; ++s) {
                 const int off = (32 * sub + li) * G::PITCH + (16 * s + 8 * lh) * 2;
-                st = mma<T>(*(const u32x4_t*)(qs + off), kreg[s], st);
-                dpt = mma<T>(*(const u32x4_t*)(dos + off), vreg[s], dpt);
+                st = mma<T>(*(const u32x4_t*)(qc + off), kreg[s], st);
+                dpt = mma<T>(*(const u32x4_t*)(dc + off), vreg[s], dpt);
             }
             float pr[16], ds[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int rl = 32 * sub + 8 * g + 4 * lh;          // local row of registers 4g .. 4g + 3
-                const f32x4_t l4 = *(const f32x4_t*)(lses + rl);
-                const f32x4_t d4 = *(const f32x4_t*)(dls + rl);
+                const f32x4_t l4 = *(const f32x4_t*)(lses[cur] + rl);
+                const f32x4_t d4 = *(const f32x4_t*)(dls[cur] + rl);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e, qi = qs0 + 8 * g + 4 * lh + e;
                     const bool vis = !CAUSAL || key <= qi;
-                    pr[r] = vis ? exp2f(c * st[r] - l4[e]) : 0.f;
+                    pr[r] = vis ? __builtin_amdgcn_exp2f(c * st[r] - l4[e]) : 0.f;
                     ds[r] = pr[r] * (dpt[r] - d4[e]);
                 }
             }
@@ -299,10 +353,17 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < G::NDB; ++db) {
-                    accv[db] = mma<T>(tr_operand<D>(dos, 32 * sub, t, 32 * db, lane), bp[t], accv[db]);
-                    acck[db] = mma<T>(tr_operand<D>(qs, 32 * sub, t, 32 * db, lane), bd[t], acck[db]);
+                    accv[db] = mma<T>(tr_operand<D>(dc, 32 * sub, t, 32 * db, lane), bp[t], accv[db]);
+                    acck[db] = mma<T>(tr_operand<D>(qc, 32 * sub, t, 32 * db, lane), bd[t], acck[db]);
                 }
         }
+        // the other buffers were last read before the previous barrier
+        if (more) {
+            qr.store(qs[cur ^ 1], tid);
+            dr.store(dos[cur ^ 1], tid);
+            store_stats(cur ^ 1);
+        }
+        __syncthreads();
     }
     store_rows<T, D>(p.dk + head, key, N, acck, p.scale, lh);
     store_rows<T, D>(p.dv + head, key, N, accv, 1.0f, lh);
