@@ -28,6 +28,9 @@ registers, spills, LDS bytes and occupancy beside the working set of
 shape, non-causal and causal (after the copy kernel, for counter runs); the
 default line carries the same figures in its "backward" object.
 
+--split times the split-KV forward (fa_fwd_split, 2-16 key ranges) against
+the plain launch on few-head long sequences (bf16, d = 128, non-causal).
+
 --standard times the standard forward of include/fa_standard.h (S and P
 materialised in HBM) on the same workload, after the copy kernel of
 --profile-run, so that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of it give
@@ -185,6 +188,52 @@ def backward_summary(steps, warmup):
     out["workload"] = ("backward with recomputation (dQ, dK, dV from O, LSE, dO), B=4 H=16 N=4096 d=128 bf16; "
                        "causal with 1% of key rows x8; 10 B H N^2 d FLOPs, halved causal")
     return out
+
+
+def split_kv(steps, warmup):
+    """Split-KV forward against the plain launch on workloads with fewer query
+    tiles than the device has CUs: bf16, d = 128, non-causal."""
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    rows = []
+    for (B, H, N) in ((1, 1, 32768), (1, 2, 16384), (1, 4, 8192), (1, 8, 4096)):
+        shape = (B, H, N, 128)
+        words = W.make_words(shape, "bf16", "normal", W.default_seed())
+        q, k, v = (upload(w, "bf16") for w in words)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        op = torch.empty((16, B, H, N, 128), dtype=torch.float32, device=q.device)
+        lp = torch.empty((16, B, H, N), dtype=torch.float32, device=q.device)
+        handle = torch.cuda.current_stream().cuda_stream
+        scale = W.scale_for(128)
+        flops = 4.0 * B * H * N * N * 128
+        res = {"B": B, "H": H, "N": N, "query_tiles": B * H * ((N + 255) // 256)}
+        for splits in (0, 2, 4, 8, 16):
+            def step():
+                if splits == 0:
+                    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N,
+                                   128, scale, 0, handle, fa.FA_DTYPE_BF16)
+                else:
+                    st = fa.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         op.data_ptr(), lp.data_ptr(), B, H, N, 128, scale, splits, handle,
+                                         fa.FA_DTYPE_BF16)
+                if st != fa.FA_OK:
+                    raise RuntimeError(fa.fa_strerror(st))
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            res["plain" if splits == 0 else f"split{splits}"] = {"ms": round(ms, 4),
+                                                                  "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+        print(json.dumps(res), flush=True)
+        del q, k, v, o, lse, op, lp
 
 
 def cpu_baseline(seconds):
@@ -447,6 +496,7 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="tile-size sweep table")
     ap.add_argument("--standard", action="store_true", help="time the standard (materialising) forward")
     ap.add_argument("--backward", action="store_true", help="time only the backward pass (fa_bwd)")
+    ap.add_argument("--split", action="store_true", help="split-KV forward against the plain one, few heads")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
                          "'trace DIR [STEPS]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
@@ -474,6 +524,9 @@ def main():
         return
     if a.standard:
         standard_baseline(a.steps, a.warmup)
+        return
+    if a.split:
+        split_kv(a.steps, a.warmup)
         return
     if a.backward:
         copy_calibration()

@@ -186,3 +186,35 @@ def test_backward_argument_checks():
     for fn in (fa.fa_bwd_bf16, fa.fa_bwd_f16):
         assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 0, 1, 1, 64, 1.0, 0, None) == fa.FA_ERR_INVALID
         assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 1, 1, 48, 1.0, 0, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_split_argument_checks():
+    OP, LP = 0x60000000, 0x70000000
+
+    def split(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, o_part=OP, lse_part=LP, B=2, H=3, N=100, d=64, scale=0.125, splits=2,
+                 stream=None, dtype=fa.FA_DTYPE_BF16)
+        a.update(over)
+        return fa.fa_fwd_split(**a)
+    assert split(B=0) == fa.FA_ERR_INVALID
+    assert split(N=-5) == fa.FA_ERR_INVALID
+    assert split(o_part=None) == fa.FA_ERR_INVALID
+    assert split(lse_part=None) == fa.FA_ERR_INVALID
+    assert split(splits=0) == fa.FA_ERR_INVALID
+    assert split(o_part=Q + 64) == fa.FA_ERR_INVALID          # work array over an input
+    assert split(lse_part=O + 16) == fa.FA_ERR_INVALID        # work array over the output
+    assert split(lse_part=OP + 1024) == fa.FA_ERR_INVALID     # the two work arrays overlap
+    assert split(scale=float("nan")) == fa.FA_ERR_INVALID
+    assert split(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert split(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert split() in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)   # valid: fails only for lack of a GPU
+
+
+def test_split_ranges_rule():
+    # whole 64-key tiles, no empty range, never more ranges than asked for
+    for N in (1, 63, 64, 65, 1000, 4096, 32768):
+        for s in (1, 2, 3, 7, 64, 1000):
+            r = fa.split_ranges(N, s)
+            assert 1 <= len(r) <= s and r[0][0] == 0 and r[-1][1] == N
+            assert all(a < b for a, b in r) and all(r[i][1] == r[i + 1][0] for i in range(len(r) - 1))
+            assert all(a % 64 == 0 for a, _ in r)

@@ -1,0 +1,87 @@
+"""GPU parity of the split-KV forward (include/fa_fwd.h ``fa_fwd_split``)
+against the float64 oracle.
+
+Each key range's partial output and log-sum-exp are themselves exact
+attention over that range's keys, so they are checked against
+``oracle.attention_ref`` on the range (the fp32 partials within the fp32
+gate G1); the merged 16-bit output and LSE are checked against the oracle
+over all keys with the gates of the plain forward (G2, LSE 1e-3).  With one
+range the merge multiplies by exp(0) = 1 and the result must equal the
+plain forward's bits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import oracle
+import tiled_exact_attention_fwd_amd as fa
+from parity_util import TOL_O, TOL_LSE, gate_errors, assert_gates, out_to64, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(shape, dtype, splits, values="normal", seed=11, scale=None):
+    words = W.make_words(shape, dtype, values, seed)
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    d = shape[3]
+    scale = W.scale_for(d) if scale is None else scale
+    o, lse, op, lp = fa.attention_split(qd, kd, vd, splits, scale=scale)
+    torch.cuda.synchronize()
+    return words, (qd, kd, vd), (o, lse, op, lp), scale
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,splits", [(1, 3), (200, 2), (1000, 3), (1000, 7), (4100, 5)])
+def test_split_matches_oracle(dtype, d, N, splits):
+    print(f"split {dtype} d={d} N={N} splits={splits}", flush=True)
+    shape = (1, 2, N, d)
+    words, _, (o, lse, op, lp), scale = run(shape, dtype, splits)
+    rng = np.random.default_rng(N)
+    rows = None if N <= 1000 else sample_rows(N, 64, rng)
+    o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
+    op_np, lp_np = out_to64(op), lp.cpu().numpy().astype(np.float64)
+    ranges = fa.split_ranges(N, splits)
+    for h in range(2):
+        vals = [W.decode64(w[0, h], dtype)[None, None] for w in words]
+        sel = slice(None) if rows is None else rows
+        o_ref, lse_ref = oracle.attention_ref(*vals, scale, False, rows=rows)
+        errs = gate_errors(None, o_np[0, h, sel][None, None], lse_np[0, h, sel][None, None], o_ref, lse_ref, dtype)
+        assert_gates(errs, dtype, f"merged N={N} splits={splits} head {h}")
+        # every range's partial is attention over that range's keys
+        for s, (k0, k1) in enumerate(ranges):
+            pr, plse = oracle.attention_ref(vals[0], vals[1][:, :, k0:k1], vals[2][:, :, k0:k1], scale, False, rows=rows)
+            e1 = float(np.max(np.abs(op_np[s, 0, h, sel] - pr[0, 0])))
+            el = float(np.max(np.abs(lp_np[s, 0, h, sel] - plse[0, 0])))
+            assert e1 <= TOL_O[dtype] and el <= TOL_LSE, (s, k0, k1, e1, el)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_range_equals_plain_forward(dtype, d):
+    shape = (2, 3, 777, d)
+    words, (qd, kd, vd), (o, lse, _, _), scale = run(shape, dtype, 1)
+    o_ref, lse_ref = fa.attention(qd, kd, vd, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lse, lse_ref)
+
+
+def test_long_few_heads_and_peaked():
+    """One long sequence of two heads (the shape split-KV is for), spiky keys
+    so that the ranges' maxima differ widely, and a negative scale."""
+    shape = (1, 2, 32768, 128)
+    for values, scale in (("spiky", None), ("normal", -0.1)):
+        print(f"split long {values} scale={scale}", flush=True)
+        words, _, (o, lse, _, _), sc = run(shape, "bf16", 8, values=values, scale=scale)
+        rng = np.random.default_rng(5)
+        rows = sample_rows(32768, 256, rng, n_random=16)
+        o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
+        for h in range(2):
+            vals = [W.decode64(w[0, h], "bf16")[None, None] for w in words]
+            o_ref, lse_ref = oracle.attention_ref(*vals, sc, False, rows=rows)
+            errs = gate_errors(None, o_np[0, h, rows][None, None], lse_np[0, h, rows][None, None], o_ref, lse_ref,
+                               "bf16")
+            assert_gates(errs, "bf16", f"long {values} head {h}")

@@ -2,7 +2,7 @@
 forward library whose C ABI is ``include/fa_fwd.h``.
 
 The functions named like the C entry points (``fa_fwd_bf16``, ``fa_fwd_f16``,
-``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_tile_shape``,
+``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_split``, ``fa_fwd_tile_shape``,
 ``fa_strerror``, ``fa_build_info``, ``fa_standard_fwd`` of
 ``include/fa_standard.h``, the materialising baseline, and ``fa_bwd_bf16``,
 ``fa_bwd_f16``, ``fa_bwd`` of ``include/fa_bwd.h``, the backward with
@@ -54,6 +54,7 @@ SIGNATURES = {
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_build_info": (ctypes.c_char_p, []),
     "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
+    "fa_fwd_split": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _I]),
     "fa_bwd_bf16": (_I, _BWD17),
     "fa_bwd_f16": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
@@ -141,6 +142,49 @@ def standard_attention(q, k, v, causal=False, scale=None):
     if st != FA_OK:
         raise FaError(st, "fa_standard_fwd")
     return o, lse, s, p
+
+
+def fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, splits, stream, dtype):
+    return lib().fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, splits, stream, dtype)
+
+
+def attention_split(q, k, v, splits, scale=None, stream=None):
+    """Split-KV forward without a mask (include/fa_fwd.h ``fa_fwd_split``):
+    returns ``(o, lse, o_part, lse_part)``, the merged outputs and the fp32
+    per-range partials ([splits, B, H, N, d] and [splits, B, H, N]; only the
+    ranges the library used are written)."""
+    import math
+    import torch
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda or t.dtype != q.dtype or t.shape != q.shape or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous device tensors of one [B, H, N, d] shape and dtype")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o_part = torch.empty((max(splits, 1), B, H, N, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((max(splits, 1), B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), o_part.data_ptr(),
+                      lse_part.data_ptr(), B, H, N, d, float(scale), int(splits), stream, dtype_code(q.dtype))
+    if st == FA_ERR_INVALID:
+        raise ValueError(f"fa_fwd_split: {fa_strerror(st)}")
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
+    return o, lse, o_part, lse_part
+
+
+def split_ranges(N, splits, tile_k=64):
+    """The key ranges fa_fwd_split uses: whole 64-key tiles, at most one range
+    per key tile (mirrors the host layer's rule; the GPU test checks the
+    partials it wrote against this)."""
+    nk = (N + tile_k - 1) // tile_k
+    want = min(splits, nk)
+    per = (nk + want - 1) // want
+    used = (nk + per - 1) // per
+    return [(s * per * tile_k, min(N, (s + 1) * per * tile_k)) for s in range(used)]
 
 
 def fa_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream):

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cfloat>
 #include <cmath>
@@ -132,6 +133,8 @@ int run(const fa_fwd_args* a) {
     const bool neg = a->scale < 0.f;
     p.qsign = neg ? (a->dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u) : 0u;
     p.counters = a->counters;
+    p.splits = 1;
+    p.split_len = a->N;
     const bool count = a->counters != nullptr;
 
     const int c = a->causal, o32 = a->out_dtype;
@@ -192,6 +195,54 @@ int run(const fa_fwd_args* a) {
     }
 }
 
+// Split-KV forward: argument checks, then the partial and merge kernels.
+int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) {
+    int st = check_args(a);
+    if (st != FA_OK) return st;
+    if (!o_part || !lse_part || splits < 1) return FA_ERR_INVALID;
+    if (a->causal || a->out_dtype || a->counters || a->tile_q || a->tile_k) return FA_ERR_UNSUPPORTED;
+    if (a->dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    const int tq = fa::tile_q16(false), tk = 64;
+    // ranges of whole key tiles; as many as asked for, at most one per key tile
+    const int nk = (a->N + tk - 1) / tk;
+    const int per = (nk + std::min(splits, nk) - 1) / std::min(splits, nk);   // key tiles per range
+    const int used = (nk + per - 1) / per;
+    const uint64_t heads = (uint64_t)a->B * a->H, tiles = heads * ((a->N + tq - 1) / tq);
+    if (tiles * used >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    const uint64_t e = elem_size(a->dtype), elems = heads * a->N * a->d;
+    const uint64_t part_b = (uint64_t)splits * elems * 4, lpart_b = (uint64_t)splits * heads * a->N * 4;
+    const void* bufs[5] = {a->q, a->k, a->v, a->o, a->lse};
+    const uint64_t bufb[5] = {elems * e, elems * e, elems * e, elems * e, heads * a->N * 4};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(o_part, part_b, bufs[i], bufb[i]) || overlaps(lse_part, lpart_b, bufs[i], bufb[i]))
+            return FA_ERR_INVALID;
+    if (overlaps(o_part, part_b, lse_part, lpart_b)) return FA_ERR_INVALID;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FA_OK) return st;
+    FwdParams p;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.o = o_part;
+    p.lse = lse_part;
+    p.N = a->N;
+    p.tiles_q = (a->N + tq - 1) / tq;
+    p.heads = (int)heads;
+    p.total = (int)tiles;
+    p.group = 1;
+    p.c = std::fmax(std::fabs(a->scale) * 1.4426950408889634f, FLT_MIN);
+    p.qsign = a->scale < 0.f ? 0x80008000u : 0u;
+    p.counters = nullptr;
+    p.splits = used;
+    p.split_len = per * tk;
+    if (a->dtype == FA_DTYPE_BF16)
+        return a->d == 64 ? fa::launch16s_bf16_d64(p, a->o, a->lse, a->stream)
+                          : fa::launch16s_bf16_d128(p, a->o, a->lse, a->stream);
+    return a->d == 64 ? fa::launch16s_f16_d64(p, a->o, a->lse, a->stream)
+                      : fa::launch16s_f16_d128(p, a->o, a->lse, a->stream);
+}
+
 fa_fwd_args plain_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                        int N, int d, float scale, int causal, void* stream, int dtype) {
     fa_fwd_args a;
@@ -227,6 +278,12 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, void* stream) {
     return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, FA_DTYPE_F32);
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* o_part, float* lse_part,
+                 int B, int H, int N, int d, float scale, int splits, void* stream, int dtype) {
+    const fa_fwd_args a = plain_args(q, k, v, o, lse, B, H, N, d, scale, 0, stream, dtype);
+    return run_split(&a, o_part, lse_part, splits);
 }
 
 int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k) {

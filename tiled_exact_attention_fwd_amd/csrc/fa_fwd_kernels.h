@@ -153,6 +153,8 @@ struct FwdParams {
     float c;            // |scale| * log2(e), at least FLT_MIN
     uint32_t qsign;     // 0x80008000 to negate Q (negative scale), else 0
     unsigned long long* counters;
+    int splits;         // split-KV launches: key ranges per query tile
+    int split_len;      // keys per range (a multiple of the key tile)
 };
 
 // Workgroup index -> (head, query tile).
@@ -293,7 +295,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // WQ (waves per workgroup, 0 = the default below) and BKT (keys per tile)
 // select other tile shapes; the library builds the defaults for every type
 // and a tile-size sweep (bf16, d = 128, no mask) besides.
-template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT, int WQ = 0, int BKT = 64>
+// SPLIT: a split-KV launch (no mask, fp32 output): workgroup b takes one
+// query tile over one range of p.split_len keys and writes that range's
+// partial output and log-sum-exp, which a second kernel merges.
+template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT, int WQ = 0, int BKT = 64, bool SPLIT = false>
 struct Fwd16 {
     // Eight waves (256 query rows, one workgroup per CU) share each K / V
     // tile copy without a mask: half the L2 -> LDS traffic of four.  Causal
@@ -325,6 +330,7 @@ struct Fwd16 {
     static constexpr int LDS = 4 * TILEB;
     static_assert(D == 64 || D == 128, "head dimension");
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile copy");
+    static_assert(!SPLIT || (!CAUSAL && OUT_F32 && !COUNT), "split-KV partials: no mask, fp32 output");
 
     // K row permutation: swap bits 2 and 3, so that each half-wave's eight
     // consecutive score registers hold eight consecutive keys
@@ -509,7 +515,20 @@ struct Fwd16 {
         unsigned long long* const counters = pin_s(p.counters);
         const float c = pin_s(p.c);
 
-        const TileId t = tile_of<CAUSAL>(blockIdx.x, p);
+        TileId t;
+        int split = 0;                              // key range of a split-KV launch
+        if constexpr (SPLIT) {
+            // (head, query tile, range), head-major so that a head's K and V
+            // are re-read from one XCD's L2
+            const int L = xcd_remap(blockIdx.x, p.total * p.splits);
+            const int per_head = p.tiles_q * p.splits;
+            t.hh = L / per_head;
+            const int rem = L - t.hh * per_head;
+            t.qi = rem / p.splits;
+            split = rem - t.qi * p.splits;
+        } else {
+            t = tile_of<CAUSAL>(blockIdx.x, p);
+        }
         const int hh = t.hh;
         const int qt0 = t.qi * BQ;
         const int q0w = qt0 + wave * 32;            // first row of this wave; lane li holds row q0w + li
@@ -517,11 +536,15 @@ struct Fwd16 {
 
         const size_t head_elems = (size_t)hh * N * D;
         const uint32_t head_bytes = (uint32_t)N * ROWB;
+        // the keys this workgroup visits: the head's, or one range of them
+        const int kfirst = SPLIT ? split * p.split_len : 0;
+        const int NK = SPLIT ? min(p.split_len, N - kfirst) : N;
+        const uint32_t kv_bytes = (uint32_t)NK * ROWB;
         const auto rq = make_rsrc((const uint8_t*)p.q + head_elems * 2, head_bytes);
-        const uint8_t* kbase = (const uint8_t*)p.k + head_elems * 2;
-        const uint8_t* vbase = (const uint8_t*)p.v + head_elems * 2;
+        const uint8_t* kbase = (const uint8_t*)p.k + head_elems * 2 + (size_t)kfirst * ROWB;
+        const uint8_t* vbase = (const uint8_t*)p.v + head_elems * 2 + (size_t)kfirst * ROWB;
 
-        const int nk = (N + BK - 1) / BK;
+        const int nk = (NK + BK - 1) / BK;
         int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
         // opaque to the optimiser: reasoning about the causal bound makes it
         // allocate the loop body with more registers than the CU holds
@@ -604,7 +627,7 @@ struct Fwd16 {
 
         // prologue: K_0 into kbuf0
         {
-            const auto rk0 = make_rsrc(kbase, head_bytes);
+            const auto rk0 = make_rsrc(kbase, kv_bytes);
 #pragma unroll
             for (int u = 0; u < LOADS; ++u) copy_part(rk0, kbuf0, wave, koff_c[u], u);
         }
@@ -632,11 +655,11 @@ struct Fwd16 {
             const bool has_sm = j >= 0 && j < wend;
             const int k0 = j * BK;
             if (has_sm) {
-                const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+                const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > NK);
                 if (need_mask) {
                     // register r of block mb holds key k0 + 8 lh + kk with the
                     // constant kk below; it is visible iff kk <= lim
-                    int lim = N - 1 - k0 - 8 * lh;
+                    int lim = NK - 1 - k0 - 8 * lh;
                     if (CAUSAL) lim = min(lim, qrow - k0 - 8 * lh);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
@@ -654,10 +677,10 @@ struct Fwd16 {
             // reads as zeros, into a buffer nobody reads before it is filled
             // again (K) or that is multiplied by zero terms (V).  Extents stay
             // below 2^30 bytes (host check), so these sums cannot wrap.
-            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : head_bytes;
-            const uint32_t vcopy = j >= 0 && j < jend ? (uint32_t)(j * TILEB) : head_bytes;
-            const auto rkt = make_rsrc(kbase + kcopy, head_bytes - kcopy);
-            const auto rvt = make_rsrc(vbase + vcopy, head_bytes - vcopy);
+            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : kv_bytes;
+            const uint32_t vcopy = j >= 0 && j < jend ? (uint32_t)(j * TILEB) : kv_bytes;
+            const auto rkt = make_rsrc(kbase + kcopy, kv_bytes - kcopy);
+            const auto rvt = make_rsrc(vbase + vcopy, kv_bytes - vcopy);
 
             // NSLOT slots; in each: its MFMA and its share of the softmax
             // stages, then the LDS operand read of slot i + PD; one 16-byte
@@ -719,10 +742,10 @@ struct Fwd16 {
             const bool odd = j & 1;
             uint8_t* kfill = odd ? kbuf1 : kbuf0;
             uint8_t* vfill = odd ? vbuf1 : vbuf0;
-            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : head_bytes;
-            const uint32_t vcopy = j < jend ? (uint32_t)(j * TILEB) : head_bytes;
-            const auto rkt = make_rsrc(kbase + kcopy, head_bytes - kcopy);
-            const auto rvt = make_rsrc(vbase + vcopy, head_bytes - vcopy);
+            const uint32_t kcopy = j + 2 < jend ? (uint32_t)((j + 2) * TILEB) : kv_bytes;
+            const uint32_t vcopy = j < jend ? (uint32_t)(j * TILEB) : kv_bytes;
+            const auto rkt = make_rsrc(kbase + kcopy, kv_bytes - kcopy);
+            const auto rvt = make_rsrc(vbase + vcopy, kv_bytes - vcopy);
 #pragma unroll
             for (int u = 0; u < LOADS; ++u) {
                 copy_part(rkt, kfill, wave, koff_c[u], u);
@@ -734,9 +757,11 @@ struct Fwd16 {
         // Lane (li, lh) holds d = 32 db + 8 jj + 4 lh + (0..3) of row q0w + li.
         const float l = st.l;
         const float inv = 1.0f / l;
+        // a split-KV launch writes range `split` of a [splits, B H, N] array
+        const size_t out_head = SPLIT ? ((size_t)split * p.heads + hh) * N : (size_t)hh * N;
         if (OUT_F32) {
             if (qrow < N) {
-                const size_t orow = head_elems + (size_t)qrow * D;
+                const size_t orow = (out_head + qrow) * D;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -794,10 +819,46 @@ struct Fwd16 {
                     }
             }
         }
-        if (lh == 0 && qrow < N) gstore(lse + (size_t)hh * N + qrow, (st.mc + __log2f(l)) * kLn2);
+        if (lh == 0 && qrow < N) gstore(lse + out_head + qrow, (st.mc + __log2f(l)) * kLn2);
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(counters, qt0, jend, N);
     }
 };
+
+// ---------------------------------------------------------------------------
+// Merge of split-KV partials.  Range s of a row holds the normalised output
+// O_s and log-sum-exp LSE_s of that row's softmax over the range's keys
+// alone.  The whole row's statistics follow from the blocked-softmax merge
+// ("Flash Attention 原理", Softmax 的分块计算; the correction factor of
+// "FlashAttention分块计算优化Transformer显存效率" §3.2): with
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+// One wave per row; a lane merges D / 64 consecutive columns.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ void __launch_bounds__(256) split_merge_kernel(const float* opart, const float* lpart, void* o,
+                                                          float* lse, int rows, int splits) {
+    constexpr int CPL = D / 64;                     // columns per lane
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;                        // whole waves; no barrier follows
+    float m = -__builtin_inff();
+    for (int s = 0; s < splits; ++s) m = fmaxf(m, lpart[(size_t)s * rows + row]);
+    float den = 0.f;
+    for (int s = 0; s < splits; ++s) den += expf(lpart[(size_t)s * rows + row] - m);
+    const float total = m + logf(den);
+    float acc[CPL] = {};
+    for (int s = 0; s < splits; ++s) {
+        const float w = expf(lpart[(size_t)s * rows + row] - total);
+        const float* src = opart + ((size_t)s * rows + row) * D + lane * CPL;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[e] += w * src[e];
+    }
+    uint16_t* dst = (uint16_t*)o + (size_t)row * D + lane * CPL;
+    if constexpr (CPL == 2) {
+        *(__attribute__((address_space(1))) uint32_t*)dst = pack2<T>(acc[0], acc[1]);
+    } else {
+        *(__attribute__((address_space(1))) uint16_t*)dst = (uint16_t)(pack2<T>(acc[0], 0.f) & 0xffffu);
+    }
+    if (lane == 0) lse[row] = total;
+}
 
 // ---------------------------------------------------------------------------
 // Persistent 16-bit kernel (16-bit output, no counters).
