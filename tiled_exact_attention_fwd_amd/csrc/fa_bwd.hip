@@ -47,6 +47,7 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     p.o = (const uint16_t*)o; p.dout = (const uint16_t*)dout; p.lse = lse;
     p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv; p.delta = delta;
     p.N = N;
+    p.heads = (int)heads;
     p.nblk = (int)nblk;
     p.c = scale * fa::bwd::kLog2e;
     p.scale = scale;

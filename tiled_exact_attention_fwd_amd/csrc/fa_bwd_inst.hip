@@ -22,11 +22,12 @@ struct bf16 { using T = BF16; };
 struct f16 { using T = F16; };
 
 template <class T, int D, bool C>
-int launch(const BwdParams& p, int heads, void* stream) {
-    const dim3 grid((unsigned)(heads * p.nblk)), block(256);
+int launch(const BwdParams& p0, int heads, void* stream) {
+    BwdParams p = p0;
+    p.nblk_k = (p.N + DkdvShape<D>::KEYS - 1) / DkdvShape<D>::KEYS;
     const hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL((dq_kernel<T, D, C>), grid, block, 0, st, p);
-    hipLaunchKernelGGL((dkdv_kernel<T, D, C>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((dq_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk_k)), dim3(DkdvShape<D>::NT), 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }  // namespace

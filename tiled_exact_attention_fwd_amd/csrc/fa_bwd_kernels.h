@@ -56,7 +56,9 @@ struct BwdParams {
     uint16_t *dq, *dk, *dv;
     float* delta;
     int N;
-    int nblk;      // 128-row blocks per head
+    int heads;     // B * H
+    int nblk;      // 128-row query blocks per head (dq_kernel)
+    int nblk_k;    // key blocks per head (dkdv_kernel, DkdvShape<D>::KEYS keys each)
     float c;       // scale * log2(e)
     float scale;
 };
@@ -92,21 +94,21 @@ struct Geo {
 // next tile are issued before the current tile is computed and stored to the
 // other LDS buffer after it, so their latency is hidden.  Rows past the head's end read as zeros through the buffer
 // resource's extent.
-template <int D>
+template <int D, int NT = 256>
 struct TileRegs {
-    static constexpr int PER = Geo<D>::CHUNKS / 256;   // 16-byte pieces per thread
+    static constexpr int PER = Geo<D>::CHUNKS / NT;    // 16-byte pieces per thread
     u32x4_t x[PER];
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int r0, int tid) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int i = tid + 256 * u, row = i / (D / 8), ch = i % (D / 8);
+            const int i = tid + NT * u, row = i / (D / 8), ch = i % (D / 8);
             x[u] = buf_load16(r, (uint32_t)(((r0 + row) * D + ch * 8) * 2));
         }
     }
     __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int i = tid + 256 * u, row = i / (D / 8), ch = i % (D / 8);
+            const int i = tid + NT * u, row = i / (D / 8), ch = i % (D / 8);
             *(u32x4_t*)(lds + row * Geo<D>::PITCH + ch * 16) = x[u];
         }
     }
@@ -121,6 +123,22 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint8_t* lds, int blk, int t
     const uint8_t* p = lds + (blk + 16 * t + 4 * lh + (s >> 2)) * G::PITCH + (col0 + 16 * (grp & 1) + 4 * (s & 3)) * 2;
     const u32x2_t a = lds_read_tr(p), b = lds_read_tr(p + 8 * G::PITCH);
     return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// Causal launches: workgroup -> (head, rank), where rank 0 is a head's most
+// expensive block.  Blocks are issued rank-major so that the launch ends with
+// the cheap ones; with a head count divisible by 8, XCD x (which runs
+// workgroups b = x mod 8) owns heads x, x + 8, ... and takes their blocks
+// rank-major, so that a head's tiles stay on one XCD's L2.
+__device__ __forceinline__ void causal_order(int bid, int heads, int& hh, int& rank) {
+    if (heads % kNumXcd == 0) {
+        const int x = bid % kNumXcd, s = bid / kNumXcd, hpx = heads / kNumXcd;
+        rank = s / hpx;
+        hh = (s - rank * hpx) * kNumXcd + x;
+    } else {
+        rank = bid / heads;
+        hh = bid - rank * heads;
+    }
 }
 
 // 16 fp32 results -> the two B operands (registers 8t .. 8t + 7 each)
@@ -157,10 +175,15 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const int N = p.N;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int hh = L / p.nblk;
-    int qb = L - hh * p.nblk;
-    if (CAUSAL) qb = p.nblk - 1 - qb;          // longest rows first
+    int hh, qb;
+    if (CAUSAL) {
+        causal_order(blockIdx.x, p.heads, hh, qb);
+        qb = p.nblk - 1 - qb;                  // the last rows see the most keys
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        hh = L / p.nblk;
+        qb = L - hh * p.nblk;
+    }
     const int q0 = qb * 128, qw = q0 + 32 * wave, q = qw + li;
     const size_t head = (size_t)hh * N * D;
     const uint32_t hb = (uint32_t)N * D * 2;
@@ -243,21 +266,43 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdParams p) {
     store_rows<T, D>(p.dq + head, q, N, acc, p.scale, lh);
 }
 
+// Shape of dkdv_kernel.  At d = 128 the accumulators of dK and dV (128
+// registers) and the K operand leave no room for V in registers at two waves
+// per SIMD, so eight waves (256 keys) share their V rows through LDS (68 KiB
+// beside the 68 KiB of Q / dO double buffers); at d = 64 four waves keep
+// both K and V in registers.
+template <int D>
+struct DkdvShape {
+    static constexpr int WAVES = D == 128 ? 8 : 4;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int KEYS = 32 * WAVES;        // keys per workgroup
+    static constexpr bool V_LDS = D == 128;
+};
+
 template <class T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(DkdvShape<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dkdv_kernel(BwdParams p) {
     using G = Geo<D>;
+    using S = DkdvShape<D>;
     // Q and dO tiles with their rows' LSE (base 2) and D, double-buffered
     __shared__ __attribute__((aligned(16))) uint8_t qs[2][G::TILE * G::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t dos[2][G::TILE * G::PITCH];
     __shared__ __attribute__((aligned(16))) float lses[2][G::TILE];
     __shared__ __attribute__((aligned(16))) float dls[2][G::TILE];
+    // the workgroup's V rows (d = 128)
+    __shared__ __attribute__((aligned(16))) uint8_t vrows[S::V_LDS ? S::KEYS * G::PITCH : 16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const int N = p.N;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int hh = L / p.nblk;
-    const int kb = L - hh * p.nblk;            // causal: block 0 sees the most queries
-    const int k0 = kb * 128, kw = k0 + 32 * wave, key = kw + li;
+    int hh, kb;                                // causal: block 0 sees the most queries
+    if (CAUSAL) {
+        causal_order(blockIdx.x, p.heads, hh, kb);
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        hh = L / p.nblk_k;
+        kb = L - hh * p.nblk_k;
+    }
+    const int k0 = kb * S::KEYS, kw = k0 + 32 * wave, key = kw + li;
     const size_t head = (size_t)hh * N * D;
     const uint32_t hb = (uint32_t)N * D * 2;
     const auto rq = make_rsrc(p.q + head, hb), rk = make_rsrc(p.k + head, hb), rv = make_rsrc(p.v + head, hb);
@@ -265,14 +310,29 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
     const float* lse = p.lse + (size_t)hh * N;
     const float* delta = p.delta + (size_t)hh * N;
 
-    // the wave's keys as B operands: lane (li, lh) holds row `key`, columns 16 s + 8 lh .. +7
-    u32x4_t kreg[G::NS], vreg[G::NS];
+    // the wave's keys as B operands: lane (li, lh) holds row `key`, columns
+    // 16 s + 8 lh .. +7 (V from LDS at d = 128)
+    u32x4_t kreg[G::NS], vreg[S::V_LDS ? 1 : G::NS];
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
         const uint32_t off = (uint32_t)((key * D + 16 * s + 8 * lh) * 2);
         kreg[s] = buf_load16(rk, off);
-        vreg[s] = buf_load16(rv, off);
+        if constexpr (!S::V_LDS) vreg[s] = buf_load16(rv, off);
     }
+    if constexpr (S::V_LDS) {
+        // rows k0 .. k0 + KEYS - 1; rows past N read as zeros
+#pragma unroll
+        for (int u = 0; u < S::KEYS * D / 8 / S::NT; ++u) {
+            const int i = tid + S::NT * u, row = i / (D / 8), ch = i % (D / 8);
+            *(u32x4_t*)(vrows + row * G::PITCH + ch * 16) = buf_load16(rv, (uint32_t)(((k0 + row) * D + ch * 8) * 2));
+        }
+    }
+    auto v_operand = [&](int s) -> u32x4_t {
+        if constexpr (S::V_LDS)
+            return *(const u32x4_t*)(vrows + (32 * wave + li) * G::PITCH + (16 * s + 8 * lh) * 2);
+        else
+            return vreg[s];
+    };
     const float c = p.c;
 
     f32x16_t acck[G::NDB], accv[G::NDB];
@@ -284,7 +344,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
 
     const int nqt = (N + G::TILE - 1) / G::TILE;
     const int qt0 = CAUSAL ? k0 / G::TILE : 0;
-    TileRegs<D> qr, dr;
+    TileRegs<D, S::NT> qr, dr;
     float lpre = 0.f, dpre = 0.f;
     // statistics of row r of tile qt: rows past N get LSE +inf, so P = 0 there
     auto load_stats = [&](int qt) {
@@ -329,7 +389,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdParams p) {
             for (int s = 0; s < G::NS; ++s) {
                 const int off = (32 * sub + li) * G::PITCH + (16 * s + 8 * lh) * 2;
                 st = mma<T>(*(const u32x4_t*)(qc + off), kreg[s], st);
-                dpt = mma<T>(*(const u32x4_t*)(dc + off), vreg[s], dpt);
+                dpt = mma<T>(*(const u32x4_t*)(dc + off), v_operand(s), dpt);
             }
             float pr[16], ds[16];
 #pragma unroll
