@@ -16,9 +16,11 @@
 //                computes S^T = K Q^T and dP^T = V dO^T (a lane holds one
 //                query), dS^T, and dQ^T += K^T dS^T; it also computes D for
 //                its rows from O and dO and writes it for the second kernel.
-//   dkdv_kernel  one workgroup = 128 keys of one head (4 waves x 32 keys);
-//                the wave's K and V rows stay in registers, Q and dO tiles of
-//                64 queries (with their LSE and D) pass through LDS.  Per
+//   dkdv_kernel  one workgroup = 256 keys of one head at d = 128 (8 waves x
+//                32 keys; 128 keys and 4 waves at d = 64); the wave's K rows
+//                stay in registers, its V rows too at d = 64 and in LDS at
+//                d = 128; Q and dO tiles of 64 queries (with their LSE and D)
+//                pass through LDS.  Per
 //                32-query block it computes S = Q K^T and dP = dO V^T (a lane
 //                holds one key), dS, and dV^T += dO^T P, dK^T += Q^T dS.
 //
