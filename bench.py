@@ -176,10 +176,13 @@ def time_backward(wl, causal, steps, warmup):
     return ms
 
 
-def backward_summary(steps, warmup):
+def backward_summary(steps, warmup, more=False):
     import fa_workloads as W
     out = {}
-    for key, name, causal in (("non_causal", "C2b", False), ("causal", "C3", True)):
+    cases = [("non_causal", "C2b", False), ("causal", "C3", True)]
+    if more:   # the ragged d = 64 workload, and fp16 at the headline shape
+        cases += [("C4_non_causal", "C4", False), ("C4_causal", "C4", True), ("C2_fp16_non_causal", "C2", False)]
+    for key, name, causal in cases:
         wl = W.WORKLOADS[name]
         ms = time_backward(wl, causal, steps, warmup)
         tf = backward_flops(wl, causal) / (ms * 1e-3) / 1e12
@@ -530,7 +533,7 @@ def main():
         return
     if a.backward:
         copy_calibration()
-        print(json.dumps({"backward": backward_summary(a.steps, a.warmup)}), flush=True)
+        print(json.dumps({"backward": backward_summary(a.steps, a.warmup, more=True)}), flush=True)
         return
 
     wl = W.WORKLOADS["C2b"]

@@ -85,3 +85,36 @@ def test_long_few_heads_and_peaked():
             errs = gate_errors(None, o_np[0, h, rows][None, None], lse_np[0, h, rows][None, None], o_ref, lse_ref,
                                "bf16")
             assert_gates(errs, "bf16", f"long {values} head {h}")
+
+
+def test_graph_replay():
+    """The split-KV call (partial and merge kernels) captured into a HIP graph
+    replays to the bits of the eager call."""
+    shape = (1, 2, 3000, 128)
+    words, (qd, kd, vd), (o_ref, l_ref, _, _), scale = run(shape, "bf16", 4)
+    B, H, N, d = shape
+    o, lse = torch.empty_like(o_ref), torch.empty_like(l_ref)
+    op = torch.empty((4, B, H, N, d), dtype=torch.float32, device=qd.device)
+    lp = torch.empty((4, B, H, N), dtype=torch.float32, device=qd.device)
+
+    def call(handle):
+        st = fa.fa_fwd_split(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), op.data_ptr(),
+                             lp.data_ptr(), B, H, N, d, scale, 4, handle, fa.FA_DTYPE_BF16)
+        assert st == fa.FA_OK
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream().cuda_stream)
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref), r
+        run(shape, "bf16", 2)
