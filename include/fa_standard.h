@@ -28,8 +28,9 @@
  *
  * Errors (fa_status of fa_fwd.h).  Every check runs before any HIP call:
  * FA_ERR_INVALID for null pointers, s or p not 16-byte aligned, B, H, N or
- * d <= 0, causal not 0 or 1, a non-finite scale; FA_ERR_UNSUPPORTED for another element type or d, or
- * sizes beyond the above.  FA_ERR_HIP if a launch fails.  The call returns
+ * d <= 0, causal not 0 or 1, a non-finite scale; FA_ERR_UNSUPPORTED for another element type or d,
+ * sizes beyond the above, or a current device that is not gfx950.  FA_ERR_HIP if the device query
+ * or a launch fails.  The call returns
  * without synchronising.
  */
 #ifndef FA_STANDARD_H

@@ -10,6 +10,7 @@
 #include "fa_bwd_kernels.h"
 #include "fa_bwd_launch.h"
 #include "fa_fwd.h"
+#include "fa_fwd_launch.h"
 
 namespace {
 
@@ -42,6 +43,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(outs[i], outb[i], outs[j], outb[j])) return FA_ERR_INVALID;
     }
+    int cus = 0;
+    const int dev_st = fa::device_check(&cus);
+    if (dev_st != FA_OK) return dev_st;
     fa::bwd::BwdParams p;
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
     p.o = (const uint16_t*)o; p.dout = (const uint16_t*)dout; p.lse = lse;

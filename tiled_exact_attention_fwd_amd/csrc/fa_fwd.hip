@@ -243,6 +243,14 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
                       : fa::launch16s_f16_d128(p, a->o, a->lse, a->stream);
 }
 
+}  // namespace
+
+// The current device's check, shared with the other host layers of the
+// library (fa_fwd_launch.h): FA_OK on gfx950, FA_ERR_UNSUPPORTED otherwise.
+int fa::device_check(int* cus) { return check_device(cus); }
+
+namespace {
+
 fa_fwd_args plain_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                        int N, int d, float scale, int causal, void* stream, int dtype) {
     fa_fwd_args a;

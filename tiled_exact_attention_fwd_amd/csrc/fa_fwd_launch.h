@@ -63,6 +63,11 @@ FA_DECLARE_TILE(256, 128)
 int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
 int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
 
+// The current device: FA_OK if it is a gfx950 (and its compute-unit count
+// in *cus), FA_ERR_UNSUPPORTED otherwise, FA_ERR_HIP if the query fails.
+// Cached per device; shared by every host layer of the library.
+int device_check(int* cus);
+
 // launch of one kernel instance on the caller's stream
 // (one workgroup per query tile, or `grid` workgroups for a persistent kernel)
 template <class K>

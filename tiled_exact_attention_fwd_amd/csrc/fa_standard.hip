@@ -24,6 +24,7 @@
 #include <cstdint>
 
 #include "fa_fwd.h"
+#include "fa_fwd_launch.h"
 #include "fa_fwd_kernels.h"
 #include "fa_standard.h"
 
@@ -233,6 +234,9 @@ extern "C" int fa_standard_fwd(const void* q, const void* k, const void* v, void
     if ((uint64_t)N * d * 2 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t blocks = (uint64_t)B * H * ((N + 3) / 4);
     if (blocks >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    int cus = 0;
+    const int dev_st = fa::device_check(&cus);
+    if (dev_st != FA_OK) return dev_st;
     const int heads = B * H;
     const hipStream_t st = (hipStream_t)stream;
     if (dtype == FA_DTYPE_BF16)
