@@ -181,3 +181,32 @@ def test_graph_replay(causal):
         for x, y in zip(outs, ref):
             assert torch.equal(x, y), r
         run_device(words, dwords, "bf16", causal, W.scale_for(128))
+
+
+@pytest.mark.parametrize("B,H,N,d", [(4, 16, 4096, 128), (3, 8, 1000, 64), (1, 24, 2100, 128), (1, 5, 700, 64)])
+def test_causal_order_writes_every_row(B, H, N, d):
+    """Outputs filled with NaN beforehand are finite everywhere afterwards:
+    the causal launch order (longest blocks first across an XCD's heads when
+    the head count is a multiple of 8, across all heads otherwise) visits
+    every block."""
+    print(f"backward causal order B={B} H={H} N={N} d={d}", flush=True)
+    words, dwords = inputs((B, H, N, d), "bf16", "normal", 13)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    dod = to_dev(dwords, "bf16")
+    o, lse = fa.attention(qd, kd, vd, causal=True, scale=W.scale_for(d))
+    outs = [torch.full_like(qd, float("nan")) for _ in range(3)]
+    delta = torch.full_like(lse, float("nan"))
+    st = fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), dod.data_ptr(),
+                   *[t.data_ptr() for t in outs], delta.data_ptr(), B, H, N, d, W.scale_for(d), 1,
+                   torch.cuda.current_stream().cuda_stream, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    for t in outs + [delta]:
+        assert bool(torch.isfinite(t).all())
+    # and one head against the oracle
+    h = (B - 1, H - 1)
+    vals = [W.decode64(w[h], "bf16")[None, None] for w in (*words, dwords)]
+    ref = oracle.attention_bwd_ref(*vals, W.scale_for(d), True)
+    dev = [out_to64(t)[h][None, None] for t in outs]
+    errs = grad_errors(dev, ref, "bf16")
+    assert max(errs.values()) <= TOL["bf16"], errs
