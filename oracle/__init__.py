@@ -30,8 +30,10 @@ Modules:
 * ``merge``      -- the P3 blocked-softmax merge on a vector.
 * ``backward``   -- ``attention_bwd_ref`` (dQ, dK, dV of the forward's
   definition by the chain rule, P materialised; the gradients the P3
-  recomputation pillar rebuilds tile by tile) and ``brute_bwd_ref`` (scalar
-  loops); pinned by finite differences of ``attention_ref``.
+  recomputation pillar rebuilds tile by tile), ``attention_bwd_sampled``
+  (the same at chosen rows of one long head, query rows taken in chunks)
+  and ``brute_bwd_ref`` (scalar loops); pinned by finite differences of
+  ``attention_ref``.
 
 Every function here is pinned by tests against values the pages print, closed
 forms, invariants, a library routine, or brute force; none is "parity
@@ -44,7 +46,7 @@ from .memory import (score_bytes, tiles_1d, score_tiles, score_tile_bytes,
                      working_set_bytes, tile_tradeoff, materialization_ratio,
                      sram_budget, sram_formula_as_printed)
 from .merge import blocked_softmax
-from .backward import attention_bwd_ref, brute_bwd_ref
+from .backward import attention_bwd_ref, attention_bwd_sampled, brute_bwd_ref
 
 __all__ = [
     "attention_ref", "attention_probs", "tiled_ref", "brute_ref",
@@ -52,5 +54,5 @@ __all__ = [
     "score_bytes", "tiles_1d", "score_tiles", "score_tile_bytes",
     "working_set_bytes", "tile_tradeoff", "materialization_ratio",
     "sram_budget", "sram_formula_as_printed", "blocked_softmax",
-    "attention_bwd_ref", "brute_bwd_ref",
+    "attention_bwd_ref", "attention_bwd_sampled", "brute_bwd_ref",
 ]

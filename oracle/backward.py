@@ -104,3 +104,35 @@ def brute_bwd_ref(q, k, v, dout, scale, causal):
                         dq[b, h, i, c] += scale * dsa * K[j][c]
                         dk[b, h, j, c] += scale * dsa * Q[i][c]
     return dq, dk, dv
+
+
+def attention_bwd_sampled(qh, kh, vh, doh, scale, causal, q_rows, k_rows, chunk=512):
+    """The same gradients for ONE head, returned only at the query rows
+    ``q_rows`` (dQ) and key rows ``k_rows`` (dK, dV), for heads too long to
+    materialise N x N matrices whole.  Query rows are taken ``chunk`` at a
+    time; every row's softmax, dP and Jacobian centring are over the complete
+    row exactly as in ``attention_bwd_ref`` (nothing is blocked along keys),
+    and the key-row gradients sum the rows' contributions.
+
+    qh, kh, vh, doh : [N, d] arrays (widened to float64).
+    Returns ``(dq [len(q_rows), d], dk [len(k_rows), d], dv [len(k_rows), d])``.
+    """
+    qh, kh, vh, doh = _as64(qh), _as64(kh), _as64(vh), _as64(doh)
+    n, d = qh.shape
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    dq = np.zeros((len(q_rows), d))
+    dk = np.zeros((len(k_rows), d))
+    dv = np.zeros((len(k_rows), d))
+    for c0 in range(0, n, chunk):
+        rows = np.arange(c0, min(c0 + chunk, n))
+        s = np.where(_visible(rows, kh.shape[0], causal), _scores(qh[rows], kh, scale), -np.inf)
+        p, _ = _softmax_rows(s)
+        dp = doh[rows] @ vh.T
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dk += scale * (ds[:, k_rows].T @ qh[rows])
+        dv += p[:, k_rows].T @ doh[rows]
+        mine = np.nonzero((q_rows >= c0) & (q_rows < c0 + len(rows)))[0]
+        if len(mine):
+            dq[mine] = scale * (ds[q_rows[mine] - c0] @ kh)
+    return dq, dk, dv

@@ -175,3 +175,18 @@ def test_planted_mistakes_are_caught(monkeypatch, variant):
     monkeypatch.setattr(obwd, "_head_grads", variant)
     bad = obwd.attention_bwd_ref(q, k, v, do, scale, True)
     assert max(float(np.max(np.abs(a - b))) for a, b in zip(bad, fd)) > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_equal_full(causal):
+    """The chunked, row-sampled form gives the full oracle's rows (chunks
+    that do not divide N, rows at chunk edges, unordered and repeated rows)."""
+    rng = np.random.default_rng(8)
+    q, k, v, do = rand4(rng, 1, 1, 53, 6)
+    full = obwd.attention_bwd_ref(q, k, v, do, 0.6, causal)
+    qr = np.array([0, 9, 10, 52, 31, 9])
+    kr = np.array([52, 0, 19, 20, 7])
+    dq, dk, dv = obwd.attention_bwd_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.6, causal, qr, kr, chunk=10)
+    np.testing.assert_allclose(dq, full[0][0, 0, qr], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(dk, full[1][0, 0, kr], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(dv, full[2][0, 0, kr], atol=1e-13, rtol=0)
