@@ -29,7 +29,8 @@ shape, non-causal and causal (after the copy kernel, for counter runs); the
 default line carries the same figures in its "backward" object.
 
 --split times the split-KV forward (fa_fwd_split, 2-16 key ranges) against
-the plain launch on few-head long sequences (bf16, d = 128, non-causal).
+the plain launch on few-head long sequences (bf16, d = 128, non-causal and
+causal).
 
 --standard times the standard forward of include/fa_standard.h (S and P
 materialised in HBM) on the same workload, after the copy kernel of
@@ -194,13 +195,14 @@ def backward_summary(steps, warmup, more=False):
 
 
 def split_kv(steps, warmup):
-    """Split-KV forward against the plain launch on workloads with fewer query
-    tiles than the device has CUs: bf16, d = 128, non-causal."""
+    """Split-KV forward against the plain launch on few-head long sequences:
+    bf16, d = 128, non-causal and causal."""
     import torch
     import fa_workloads as W
     import tiled_exact_attention_fwd_amd as fa
     rows = []
-    for (B, H, N) in ((1, 1, 32768), (1, 2, 16384), (1, 4, 8192), (1, 8, 4096)):
+    for (B, H, N, causal) in ((1, 1, 32768, 0), (1, 2, 16384, 0), (1, 4, 8192, 0), (1, 8, 4096, 0),
+                              (1, 1, 32768, 1), (1, 4, 32768, 1), (1, 8, 16384, 1), (1, 32, 32768, 1)):
         shape = (B, H, N, 128)
         words = W.make_words(shape, "bf16", "normal", W.default_seed())
         q, k, v = (upload(w, "bf16") for w in words)
@@ -210,16 +212,17 @@ def split_kv(steps, warmup):
         lp = torch.empty((16, B, H, N), dtype=torch.float32, device=q.device)
         handle = torch.cuda.current_stream().cuda_stream
         scale = W.scale_for(128)
-        flops = 4.0 * B * H * N * N * 128
-        res = {"B": B, "H": H, "N": N, "query_tiles": B * H * ((N + 255) // 256)}
+        flops = 4.0 * B * H * N * N * 128 / (2 if causal else 1)
+        tq = 128 if causal else 256
+        res = {"B": B, "H": H, "N": N, "causal": bool(causal), "query_tiles": B * H * ((N + tq - 1) // tq)}
         for splits in (0, 2, 4, 8, 16):
             def step():
                 if splits == 0:
                     st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N,
-                                   128, scale, 0, handle, fa.FA_DTYPE_BF16)
+                                   128, scale, causal, handle, fa.FA_DTYPE_BF16)
                 else:
                     st = fa.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                         op.data_ptr(), lp.data_ptr(), B, H, N, 128, scale, splits, handle,
+                                         op.data_ptr(), lp.data_ptr(), B, H, N, 128, scale, causal, splits, handle,
                                          fa.FA_DTYPE_BF16)
                 if st != fa.FA_OK:
                     raise RuntimeError(fa.fa_strerror(st))

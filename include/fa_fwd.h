@@ -143,19 +143,22 @@ typedef struct {
 int fa_fwd_ex(const fa_fwd_args* args);
 
 /*
- * Split-KV forward (no mask, 16-bit inputs): the keys of every head are cut
- * into `splits` ranges of whole 64-key tiles (fewer when N has fewer key
- * tiles), each (query tile, key range) runs as its own workgroup and writes
- * the partial output and log-sum-exp of its range's softmax in fp32, and a
+ * Split-KV forward (16-bit inputs): the keys of every head are cut into
+ * `splits` ranges of whole 64-key tiles (fewer when N has fewer key tiles),
+ * each (query tile, key range) runs as its own workgroup and writes the
+ * partial output and log-sum-exp of its range's softmax in fp32, and a
  * second kernel merges the ranges of every row with the blocked-softmax rule
  * of "Flash Attention 原理" (Softmax 的分块计算) -- the correction factor of
  * §3.2 of "FlashAttention分块计算优化Transformer显存效率" applied once per
- * range: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  Same
- * result as fa_fwd up to rounding; it fills the device when B * H * N is
- * too small for one workgroup per query tile to do so.
+ * range: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  Under
+ * the causal mask a range with no key visible to a row contributes O = 0,
+ * LSE = -inf (weight 0).  Same result as fa_fwd up to rounding; it fills the
+ * device when B * H * N is too small for one workgroup per query tile to do
+ * so, and under the mask it cuts the longest rows into pieces.
  *   o, lse     outputs, as for fa_fwd
  *   o_part     device work array of splits * B * H * N * d fp32
  *   lse_part   device work array of splits * B * H * N fp32
+ *   causal     as for fa_fwd
  *   splits     key ranges requested, >= 1
  *   dtype      FA_DTYPE_BF16 or FA_DTYPE_F16
  * The caller allocates the work arrays; they must not overlap any input,
@@ -164,7 +167,7 @@ int fa_fwd_ex(const fa_fwd_args* args);
  */
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                  float* o_part, float* lse_part, int B, int H, int N, int d,
-                 float scale, int splits, void* stream, int dtype);
+                 float scale, int causal, int splits, void* stream, int dtype);
 
 /*
  * The (tile_q, tile_k) shape a launch with these parameters uses by default,

@@ -192,8 +192,8 @@ def test_split_argument_checks():
     OP, LP = 0x60000000, 0x70000000
 
     def split(**over):
-        a = dict(q=Q, k=K, v=V, o=O, lse=L, o_part=OP, lse_part=LP, B=2, H=3, N=100, d=64, scale=0.125, splits=2,
-                 stream=None, dtype=fa.FA_DTYPE_BF16)
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, o_part=OP, lse_part=LP, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+                 splits=2, stream=None, dtype=fa.FA_DTYPE_BF16)
         a.update(over)
         return fa.fa_fwd_split(**a)
     assert split(B=0) == fa.FA_ERR_INVALID
@@ -207,7 +207,9 @@ def test_split_argument_checks():
     assert split(scale=float("nan")) == fa.FA_ERR_INVALID
     assert split(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
     assert split(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert split(causal=2) == fa.FA_ERR_INVALID
     assert split() in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)   # valid: fails only for lack of a GPU
+    assert split(causal=1) in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)
 
 
 def test_split_ranges_rule():

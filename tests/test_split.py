@@ -22,23 +22,24 @@ from parity_util import TOL_O, TOL_LSE, gate_errors, assert_gates, out_to64, sam
 pytestmark = pytest.mark.gpu
 
 
-def run(shape, dtype, splits, values="normal", seed=11, scale=None):
+def run(shape, dtype, splits, values="normal", seed=11, scale=None, causal=False):
     words = W.make_words(shape, dtype, values, seed)
     qd, kd, vd = (to_dev(w, dtype) for w in words)
     d = shape[3]
     scale = W.scale_for(d) if scale is None else scale
-    o, lse, op, lp = fa.attention_split(qd, kd, vd, splits, scale=scale)
+    o, lse, op, lp = fa.attention_split(qd, kd, vd, splits, causal=causal, scale=scale)
     torch.cuda.synchronize()
     return words, (qd, kd, vd), (o, lse, op, lp), scale
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,splits", [(1, 3), (200, 2), (1000, 3), (1000, 7), (4100, 5)])
-def test_split_matches_oracle(dtype, d, N, splits):
-    print(f"split {dtype} d={d} N={N} splits={splits}", flush=True)
+def test_split_matches_oracle(dtype, d, causal, N, splits):
+    print(f"split {dtype} d={d} causal={causal} N={N} splits={splits}", flush=True)
     shape = (1, 2, N, d)
-    words, _, (o, lse, op, lp), scale = run(shape, dtype, splits)
+    words, _, (o, lse, op, lp), scale = run(shape, dtype, splits, causal=causal)
     rng = np.random.default_rng(N)
     rows = None if N <= 1000 else sample_rows(N, 64, rng)
     o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
@@ -47,9 +48,16 @@ def test_split_matches_oracle(dtype, d, N, splits):
     for h in range(2):
         vals = [W.decode64(w[0, h], dtype)[None, None] for w in words]
         sel = slice(None) if rows is None else rows
-        o_ref, lse_ref = oracle.attention_ref(*vals, scale, False, rows=rows)
+        o_ref, lse_ref = oracle.attention_ref(*vals, scale, causal, rows=rows)
         errs = gate_errors(None, o_np[0, h, sel][None, None], lse_np[0, h, sel][None, None], o_ref, lse_ref, dtype)
-        assert_gates(errs, dtype, f"merged N={N} splits={splits} head {h}")
+        assert_gates(errs, dtype, f"merged N={N} splits={splits} causal={causal} head {h}")
+        if causal:
+            # a range that starts after a row holds none of its keys: O = 0, LSE = -inf
+            qrows = np.arange(N) if rows is None else rows
+            for s, (k0, k1) in enumerate(ranges):
+                blind = qrows[qrows < k0]
+                assert np.all(np.isneginf(lp_np[s, 0, h, blind])) and np.all(op_np[s, 0, h, blind] == 0)
+            continue
         # every range's partial is attention over that range's keys
         for s, (k0, k1) in enumerate(ranges):
             pr, plse = oracle.attention_ref(vals[0], vals[1][:, :, k0:k1], vals[2][:, :, k0:k1], scale, False, rows=rows)
@@ -60,10 +68,11 @@ def test_split_matches_oracle(dtype, d, N, splits):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_one_range_equals_plain_forward(dtype, d):
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_range_equals_plain_forward(dtype, d, causal):
     shape = (2, 3, 777, d)
-    words, (qd, kd, vd), (o, lse, _, _), scale = run(shape, dtype, 1)
-    o_ref, lse_ref = fa.attention(qd, kd, vd, causal=False, scale=scale)
+    words, (qd, kd, vd), (o, lse, _, _), scale = run(shape, dtype, 1, causal=causal)
+    o_ref, lse_ref = fa.attention(qd, kd, vd, causal=causal, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
     assert torch.equal(lse, lse_ref)
@@ -71,17 +80,18 @@ def test_one_range_equals_plain_forward(dtype, d):
 
 def test_long_few_heads_and_peaked():
     """One long sequence of two heads (the shape split-KV is for), spiky keys
-    so that the ranges' maxima differ widely, and a negative scale."""
+    so that the ranges' maxima differ widely, a negative scale, and the
+    causal mask."""
     shape = (1, 2, 32768, 128)
-    for values, scale in (("spiky", None), ("normal", -0.1)):
-        print(f"split long {values} scale={scale}", flush=True)
-        words, _, (o, lse, _, _), sc = run(shape, "bf16", 8, values=values, scale=scale)
+    for values, scale, causal in (("spiky", None, False), ("normal", -0.1, False), ("half", None, True)):
+        print(f"split long {values} scale={scale} causal={causal}", flush=True)
+        words, _, (o, lse, _, _), sc = run(shape, "bf16", 8, values=values, scale=scale, causal=causal)
         rng = np.random.default_rng(5)
         rows = sample_rows(32768, 256, rng, n_random=16)
         o_np, lse_np = out_to64(o), lse.cpu().numpy().astype(np.float64)
         for h in range(2):
             vals = [W.decode64(w[0, h], "bf16")[None, None] for w in words]
-            o_ref, lse_ref = oracle.attention_ref(*vals, sc, False, rows=rows)
+            o_ref, lse_ref = oracle.attention_ref(*vals, sc, causal, rows=rows)
             errs = gate_errors(None, o_np[0, h, rows][None, None], lse_np[0, h, rows][None, None], o_ref, lse_ref,
                                "bf16")
             assert_gates(errs, "bf16", f"long {values} head {h}")
@@ -99,7 +109,7 @@ def test_graph_replay():
 
     def call(handle):
         st = fa.fa_fwd_split(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), op.data_ptr(),
-                             lp.data_ptr(), B, H, N, d, scale, 4, handle, fa.FA_DTYPE_BF16)
+                             lp.data_ptr(), B, H, N, d, scale, 0, 4, handle, fa.FA_DTYPE_BF16)
         assert st == fa.FA_OK
 
     side = torch.cuda.Stream()

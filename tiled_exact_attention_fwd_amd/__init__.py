@@ -54,7 +54,7 @@ SIGNATURES = {
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_build_info": (ctypes.c_char_p, []),
     "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
-    "fa_fwd_split": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _P, _I]),
+    "fa_fwd_split": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _I, _P, _I]),
     "fa_bwd_bf16": (_I, _BWD17),
     "fa_bwd_f16": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
@@ -144,12 +144,12 @@ def standard_attention(q, k, v, causal=False, scale=None):
     return o, lse, s, p
 
 
-def fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, splits, stream, dtype):
-    return lib().fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, splits, stream, dtype)
+def fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, causal, splits, stream, dtype):
+    return lib().fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, causal, splits, stream, dtype)
 
 
-def attention_split(q, k, v, splits, scale=None, stream=None):
-    """Split-KV forward without a mask (include/fa_fwd.h ``fa_fwd_split``):
+def attention_split(q, k, v, splits, causal=False, scale=None, stream=None):
+    """Split-KV forward (include/fa_fwd.h ``fa_fwd_split``):
     returns ``(o, lse, o_part, lse_part)``, the merged outputs and the fp32
     per-range partials ([splits, B, H, N, d] and [splits, B, H, N]; only the
     ranges the library used are written)."""
@@ -168,7 +168,8 @@ def attention_split(q, k, v, splits, scale=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), o_part.data_ptr(),
-                      lse_part.data_ptr(), B, H, N, d, float(scale), int(splits), stream, dtype_code(q.dtype))
+                      lse_part.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), int(splits), stream,
+                      dtype_code(q.dtype))
     if st == FA_ERR_INVALID:
         raise ValueError(f"fa_fwd_split: {fa_strerror(st)}")
     if st != FA_OK:

@@ -200,9 +200,10 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
     int st = check_args(a);
     if (st != FA_OK) return st;
     if (!o_part || !lse_part || splits < 1) return FA_ERR_INVALID;
-    if (a->causal || a->out_dtype || a->counters || a->tile_q || a->tile_k) return FA_ERR_UNSUPPORTED;
+    if (a->out_dtype || a->counters || a->tile_q || a->tile_k) return FA_ERR_UNSUPPORTED;
     if (a->dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
-    const int tq = fa::tile_q16(false), tk = 64;
+    const bool causal = a->causal != 0;
+    const int tq = fa::tile_q16(causal), tk = 64;
     // ranges of whole key tiles; as many as asked for, at most one per key tile
     const int nk = (a->N + tk - 1) / tk;
     const int per = (nk + std::min(splits, nk) - 1) / std::min(splits, nk);   // key tiles per range
@@ -236,11 +237,16 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
     p.counters = nullptr;
     p.splits = used;
     p.split_len = per * tk;
-    if (a->dtype == FA_DTYPE_BF16)
-        return a->d == 64 ? fa::launch16s_bf16_d64(p, a->o, a->lse, a->stream)
-                          : fa::launch16s_bf16_d128(p, a->o, a->lse, a->stream);
-    return a->d == 64 ? fa::launch16s_f16_d64(p, a->o, a->lse, a->stream)
-                      : fa::launch16s_f16_d128(p, a->o, a->lse, a->stream);
+    const bool bf = a->dtype == FA_DTYPE_BF16, d64 = a->d == 64;
+    if (causal)
+        return bf ? (d64 ? fa::launch16s_bf16_d64_c1(p, a->o, a->lse, a->stream)
+                         : fa::launch16s_bf16_d128_c1(p, a->o, a->lse, a->stream))
+                  : (d64 ? fa::launch16s_f16_d64_c1(p, a->o, a->lse, a->stream)
+                         : fa::launch16s_f16_d128_c1(p, a->o, a->lse, a->stream));
+    return bf ? (d64 ? fa::launch16s_bf16_d64_c0(p, a->o, a->lse, a->stream)
+                     : fa::launch16s_bf16_d128_c0(p, a->o, a->lse, a->stream))
+              : (d64 ? fa::launch16s_f16_d64_c0(p, a->o, a->lse, a->stream)
+                     : fa::launch16s_f16_d128_c0(p, a->o, a->lse, a->stream));
 }
 
 }  // namespace
@@ -289,8 +295,8 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, float* o_part, float* lse_part,
-                 int B, int H, int N, int d, float scale, int splits, void* stream, int dtype) {
-    const fa_fwd_args a = plain_args(q, k, v, o, lse, B, H, N, d, scale, 0, stream, dtype);
+                 int B, int H, int N, int d, float scale, int causal, int splits, void* stream, int dtype) {
+    const fa_fwd_args a = plain_args(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
     return run_split(&a, o_part, lse_part, splits);
 }
 

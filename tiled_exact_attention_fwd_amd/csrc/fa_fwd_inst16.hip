@@ -31,13 +31,11 @@ int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
                  : launch_kernel<Fwd16<T, FA_INST_D, C, false, false>>(p, stream);
 }
 
-#define FA_CAT4(a, b, c, d) a##b##c##d
-#define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
-#if FA_INST_C == 0
 // split-KV: partials over key ranges (per-tile kernel, fp32 output), then the merge
-int FA_XCAT4(launch16s_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, void* o, float* lse, void* stream) {
-    using K = Fwd16<FA_TYPE(FA_INST_T), FA_INST_D, false, true, false, 0, 64, true>;
-    static_assert(K::BQ == tile_q16(false) && K::BK == 64, "grid tile");
+int FA_XCAT6(launch16s_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)(const FwdParams& p, void* o, float* lse,
+                                                                   void* stream) {
+    using K = Fwd16<FA_TYPE(FA_INST_T), FA_INST_D, FA_INST_C != 0, true, false, 0, 64, true>;
+    static_assert(K::BQ == tile_q16(FA_INST_C != 0) && K::BK == 64, "grid tile");
     void* args[] = {const_cast<FwdParams*>(&p)};
     hipError_t err = hipLaunchKernel((const void*)&fwd_kernel<K>, dim3(p.total * p.splits), dim3(K::NT), args, 0,
                                      (hipStream_t)stream);
@@ -47,6 +45,10 @@ int FA_XCAT4(launch16s_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, void* o, 
                        (hipStream_t)stream, (const float*)p.o, (const float*)p.lse, o, lse, rows, p.splits);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+#define FA_CAT4(a, b, c, d) a##b##c##d
+#define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
+#if FA_INST_C == 0
 // the persistent kernel (no mask, 16-bit output, no counters) on `grid` workgroups
 int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>::BQ == tile_q16(false), "grid tile");

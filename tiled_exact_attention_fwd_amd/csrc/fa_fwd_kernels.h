@@ -295,9 +295,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // WQ (waves per workgroup, 0 = the default below) and BKT (keys per tile)
 // select other tile shapes; the library builds the defaults for every type
 // and a tile-size sweep (bf16, d = 128, no mask) besides.
-// SPLIT: a split-KV launch (no mask, fp32 output): workgroup b takes one
-// query tile over one range of p.split_len keys and writes that range's
-// partial output and log-sum-exp, which a second kernel merges.
+// SPLIT: a split-KV launch (fp32 output): workgroup b takes one query tile
+// over one range of p.split_len keys and writes that range's partial output
+// and log-sum-exp, which a second kernel merges.  Under the causal mask a
+// range may hold no key visible to a row (or to the whole tile): that row's
+// partial is O = 0 with LSE = -inf, which the merge weights by exp(-inf) = 0.
 template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT, int WQ = 0, int BKT = 64, bool SPLIT = false>
 struct Fwd16 {
     // Eight waves (256 query rows, one workgroup per CU) share each K / V
@@ -330,7 +332,7 @@ struct Fwd16 {
     static constexpr int LDS = 4 * TILEB;
     static_assert(D == 64 || D == 128, "head dimension");
     static_assert(LOADS >= 1 && TILEB % (NT * 16) == 0, "tile copy");
-    static_assert(!SPLIT || (!CAUSAL && OUT_F32 && !COUNT), "split-KV partials: no mask, fp32 output");
+    static_assert(!SPLIT || (OUT_F32 && !COUNT), "split-KV partials: fp32 output, no counters");
 
     // K row permutation: swap bits 2 and 3, so that each half-wave's eight
     // consecutive score registers hold eight consecutive keys
@@ -517,7 +519,17 @@ struct Fwd16 {
 
         TileId t;
         int split = 0;                              // key range of a split-KV launch
-        if constexpr (SPLIT) {
+        if constexpr (SPLIT && CAUSAL) {
+            // (query tile, head, range), longest tiles first: consecutive
+            // workgroups go to different XCDs, so every XCD gets its share
+            // of the long tiles (a head-major order would hand one XCD all
+            // of a head's last, longest tiles)
+            const int per_rank = p.heads * p.splits;
+            const int rank = blockIdx.x / per_rank, rem = blockIdx.x - rank * per_rank;
+            t.qi = p.tiles_q - 1 - rank;
+            t.hh = rem / p.splits;
+            split = rem - t.hh * p.splits;
+        } else if constexpr (SPLIT) {
             // (head, query tile, range), head-major so that a head's K and V
             // are re-read from one XCD's L2
             const int L = xcd_remap(blockIdx.x, p.total * p.splits);
@@ -545,12 +557,25 @@ struct Fwd16 {
         const uint8_t* vbase = (const uint8_t*)p.v + head_elems * 2 + (size_t)kfirst * ROWB;
 
         const int nk = (NK + BK - 1) / BK;
-        int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        int jend;
+        if constexpr (SPLIT && CAUSAL) {
+            // the last key of the tile's last row, relative to the range
+            const int kmax = min(qt0 + BQ, N) - 1 - kfirst;
+            jend = kmax < 0 ? 0 : min(nk, kmax / BK + 1);
+        } else {
+            jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        }
         // opaque to the optimiser: reasoning about the causal bound makes it
         // allocate the loop body with more registers than the CU holds
         asm volatile("" : "+s"(jend));
         // key tiles this wave computes (all of them, up to its diagonal when causal)
-        int wend = q0w < N ? (CAUSAL ? min(jend, (q0w + 31) / BK + 1) : jend) : 0;
+        int wend;
+        if constexpr (SPLIT && CAUSAL) {
+            const int wmax = q0w + 31 - kfirst;     // this wave's last visible key, relative
+            wend = q0w < N ? (wmax < 0 ? 0 : min(jend, wmax / BK + 1)) : 0;
+        } else {
+            wend = q0w < N ? (CAUSAL ? min(jend, (q0w + 31) / BK + 1) : jend) : 0;
+        }
         wend = __builtin_amdgcn_readfirstlane(wend);
 
         // (All of a wave's own LDS writes -- this zero fill, the output
@@ -655,12 +680,12 @@ struct Fwd16 {
             const bool has_sm = j >= 0 && j < wend;
             const int k0 = j * BK;
             if (has_sm) {
-                const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > NK);
+                const bool need_mask = (CAUSAL && kfirst + k0 + BK - 1 > q0w) || (k0 + BK > NK);
                 if (need_mask) {
                     // register r of block mb holds key k0 + 8 lh + kk with the
                     // constant kk below; it is visible iff kk <= lim
                     int lim = NK - 1 - k0 - 8 * lh;
-                    if (CAUSAL) lim = min(lim, qrow - k0 - 8 * lh);
+                    if (CAUSAL) lim = min(lim, qrow - kfirst - k0 - 8 * lh);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -756,7 +781,8 @@ struct Fwd16 {
         // epilogue: O = O_running / l, LSE = ln(sum exp(scale * S)) = (mc + log2 l) ln 2.
         // Lane (li, lh) holds d = 32 db + 8 jj + 4 lh + (0..3) of row q0w + li.
         const float l = st.l;
-        const float inv = 1.0f / l;
+        // (a split-KV row that sees no key of its range: l = 0, O = 0, LSE = -inf)
+        const float inv = SPLIT ? (l > 0.f ? 1.0f / l : 0.f) : 1.0f / l;
         // a split-KV launch writes range `split` of a [splits, B H, N] array
         const size_t out_head = SPLIT ? ((size_t)split * p.heads + hh) * N : (size_t)hh * N;
         if (OUT_F32) {
@@ -819,7 +845,8 @@ struct Fwd16 {
                     }
             }
         }
-        if (lh == 0 && qrow < N) gstore(lse + out_head + qrow, (st.mc + __log2f(l)) * kLn2);
+        if (lh == 0 && qrow < N)
+            gstore(lse + out_head + qrow, SPLIT && !(l > 0.f) ? -__builtin_inff() : (st.mc + __log2f(l)) * kLn2);
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(counters, qt0, jend, N);
     }
 };

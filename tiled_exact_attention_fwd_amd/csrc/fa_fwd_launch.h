@@ -42,12 +42,19 @@ constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TIL
 // causal persistent kernels (d = 64; an even number of query tiles, paired)
 int launch16pc_bf16_d64(const FwdParams& p, int grid, void* stream);
 int launch16pc_f16_d64(const FwdParams& p, int grid, void* stream);
-// split-KV launches (no mask): p.o / p.lse point at the fp32 partials
-// ([p.splits, B H, N] x d and [p.splits, B H, N]); the merge writes o and lse
-int launch16s_bf16_d64(const FwdParams& p, void* o, float* lse, void* stream);
-int launch16s_bf16_d128(const FwdParams& p, void* o, float* lse, void* stream);
-int launch16s_f16_d64(const FwdParams& p, void* o, float* lse, void* stream);
-int launch16s_f16_d128(const FwdParams& p, void* o, float* lse, void* stream);
+// split-KV launches: p.o / p.lse point at the fp32 partials ([p.splits,
+// B H, N] x d and [p.splits, B H, N]); the merge writes o and lse
+#define FA_DECLARE16S(T, D, C) \
+    int launch16s_##T##_d##D##_c##C(const FwdParams& p, void* o, float* lse, void* stream);
+FA_DECLARE16S(bf16, 64, 0)
+FA_DECLARE16S(bf16, 64, 1)
+FA_DECLARE16S(bf16, 128, 0)
+FA_DECLARE16S(bf16, 128, 1)
+FA_DECLARE16S(f16, 64, 0)
+FA_DECLARE16S(f16, 64, 1)
+FA_DECLARE16S(f16, 128, 0)
+FA_DECLARE16S(f16, 128, 1)
+#undef FA_DECLARE16S
 // tile-size sweep (bf16, d = 128, no mask): every (query rows, keys) in
 // {64, 128, 256} x {32, 64, 128} besides the default 256 x 64
 #define FA_DECLARE_TILE(Q, K) int launch16t_q##Q##_k##K(const FwdParams& p, bool count, void* stream);
