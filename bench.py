@@ -131,6 +131,82 @@ def time_workload(wl, causal, steps, warmup):
                 launch_median_ms=per[len(per) // 2], launch_min_ms=per[0])
 
 
+def clock_and_cold(wl, seconds=1.5, cold_reps=20):
+    """Two side measurements of the headline launch.
+
+    clock: the shader clock (SCLK) that rocm-smi reports, sampled by a side
+    thread while the launch repeats for about `seconds`; the matrix-core peak
+    at that clock is CUs x 4096 FLOP/clk x SCLK (dense 16-bit MFMA), next to
+    the vendor's 2.4 GHz figure.  cold_cache: each launch timed alone after
+    writing a 512 MiB buffer (more than the 256 MB memory-side cache), so
+    that Q, K and V come from HBM."""
+    import re
+    import subprocess
+    import threading
+    import torch
+    import fa_workloads as W
+    import tiled_exact_attention_fwd_amd as fa
+    words = W.make_words(wl.shape, wl.dtype, wl.values, W.default_seed())
+    q, k, v = (upload(w, wl.dtype) for w in words)
+    o = torch.empty_like(q)
+    lse = torch.empty(wl.shape[:3], dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    B, H, N, d = wl.shape
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+            W.scale_for(d), 0, stream.cuda_stream, fa.dtype_code(q.dtype))
+
+    def step():
+        if fa.fa_fwd(*args) != fa.FA_OK:
+            raise RuntimeError("fa_fwd failed")
+
+    for _ in range(50):
+        step()
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+                samples.extend(int(m.group(1)) for m in re.finditer(r'"sclk clock speed:"\s*:\s*"\(?(\d+)Mhz', r.stdout))
+            except (OSError, subprocess.SubprocessError):
+                return
+            stop.wait(0.05)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(100):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    clock = None
+    if samples:
+        mhz = sum(samples) / len(samples)
+        clock = {"sclk_mhz_mean": round(mhz, 1), "samples": len(samples), "cus": cus,
+                 "mfma_peak_at_clock": round(cus * 4096 * mhz * 1e6 / 1e12, 1),
+                 "mfma_peak_at_2400mhz": round(cus * 4096 * 2.4e9 / 1e12, 1), "source": "rocm-smi --showclocks"}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    per = []
+    for _ in range(cold_reps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    per.sort()
+    cold = {"median_ms": round(per[len(per) // 2], 5), "min_ms": round(per[0], 5),
+            "TFLOP/s": round(wl.flops(False) / (per[len(per) // 2] * 1e-3) / 1e12, 2),
+            "how": "each launch timed alone after writing a 512 MiB buffer"}
+    del q, k, v, o, lse, flush
+    return clock, cold
+
+
 def backward_flops(wl, causal):
     """10 B H N^2 d: the five N x N x d products of the backward (recomputed
     S, dP, dV, dK, dQ), 2.5 times the forward's convention, halved causal.
@@ -314,23 +390,27 @@ def summarize(kind, paths):
             return list(csv.DictReader(f))
 
     if kind == "trace":
-        # the last `last` dispatches of a kernel are the launches the bench
-        # times one by one (its launch_ms)
-        last = int(paths[1]) if len(paths) > 1 else 100
+        # 'trace DIR [K [S]]': the K dispatches of a kernel after the first S
+        # (default: its last K) -- for the headline kernel, S = 200 and K = 100
+        # are the launches the bench times one by one (its launch_ms)
+        count = int(paths[1]) if len(paths) > 1 else 100
+        skip = int(paths[2]) if len(paths) > 2 else None
         durs = {}
         for r in sorted(rows(paths[0], "*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
             durs.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        print(f"| kernel | calls | average us | min us | max us | average of the last {last} us |")
+        label = f"last {count}" if skip is None else f"dispatches {skip + 1}-{skip + count}"
+        print(f"| kernel | calls | average us | min us | max us | average of the {label} us |")
         print("|---|---|---|---|---|---|")
         for r in rows(paths[0], "*kernel_stats.csv"):
             name = r["Name"]
             if "fa::" not in name:
                 continue
-            tail = durs.get(name, [])[-last:]
-            tail_avg = f"{sum(tail) / len(tail):.1f}" if tail else "-"
+            d = durs.get(name, [])
+            sel = d[-count:] if skip is None else d[skip:skip + count]
+            avg = f"{sum(sel) / len(sel):.1f}" if sel else "-"
             print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {tail_avg} |")
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {avg} |")
         return
     if kind == "l2":
         hits, misses = {}, {}
@@ -505,7 +585,7 @@ def main():
     ap.add_argument("--split", action="store_true", help="split-KV forward against the plain one, few heads")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
-                         "'trace DIR [STEPS]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
+                         "'trace DIR [COUNT [SKIP]]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
     a = ap.parse_args()
     if a.summarize:
         summarize(a.summarize[0], a.summarize[1:])
@@ -551,6 +631,9 @@ def main():
     causal_value = fc / (rc["ms_per_step"] * 1e-3) / 1e12
 
     bwd = backward_summary(max(10, a.steps // 4), max(5, a.warmup // 4))
+    clock, cold = clock_and_cold(wl)
+    if clock:
+        clock["frac_at_clock"] = round(achieved / clock["mfma_peak_at_clock"], 4)
     traffic = traffic_for_kernel()
     out = {
         "metric": METRIC,
@@ -577,6 +660,8 @@ def main():
                    "ms_per_step": round(rc["ms_per_step"], 5),
                    "frac": round(fc / (rc["launch_mean_ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)},
         "backward": bwd,
+        "clock": clock,
+        "cold_cache": cold,
         "launch_ms": {"mean": round(r["launch_mean_ms"], 5), "median": round(r["launch_median_ms"], 5),
                       "min": round(r["launch_min_ms"], 5)},
         "hbm_min_gbs": round((4 * wl.B * wl.H * wl.N * wl.d * 2 + 4 * wl.B * wl.H * wl.N)
