@@ -238,3 +238,23 @@ def test_long_context_sampled_rows():
     assert max(errs.values()) <= TOL[wl.dtype], errs
     colsum = dk.float().sum(dim=2).abs().max().item()
     assert colsum <= TOL[wl.dtype] * dk.float().abs().max().item() * N ** 0.5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_and_negative_scale(causal):
+    """scale 0: P is uniform over the visible keys, so dQ = dK = 0 exactly
+    (they carry the factor scale) and dV[k] is the mean-weighted sum of dO
+    over the queries that see k (the oracle's closed form); a negative scale
+    against the oracle."""
+    words, dwords = inputs((1, 3, 150, 64), "bf16", "normal", 14)
+    for scale in (0.0, -0.2):
+        (_, _, _, _, _, _), (dq, dk, dv, _) = run_device(words, dwords, "bf16", causal, scale)
+        vals = [W.decode64(w, "bf16") for w in (*words, dwords)]
+        ref = oracle.attention_bwd_ref(*vals, scale, causal)
+        dev = [out_to64(t) for t in (dq, dk, dv)]
+        if scale == 0.0:
+            assert not dq.any() and not dk.any()
+            errs = grad_errors(dev[2:], ref[2:], "bf16")
+        else:
+            errs = grad_errors(dev, ref, "bf16")
+        assert max(errs.values()) <= TOL["bf16"], (scale, errs)
