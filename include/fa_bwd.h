@@ -43,7 +43,7 @@
  * FA_ERR_INVALID for a null pointer, B, H, N or d <= 0, causal not 0 or 1, a
  * non-finite scale, or an output overlapping an input or another output;
  * FA_ERR_UNSUPPORTED for fp32 (no backward kernel is built for it), d other
- * than 64 or 128, a head of 2^31 bytes or more, a grid beyond 2^31
+ * than 64 or 128, N * d * 4 of 2^31 or more (as for fa_fwd), a grid beyond 2^31
  * workgroups, or a current device that is not gfx950; FA_ERR_HIP if the
  * device query or a launch fails.  Faults inside a kernel surface
  * at the caller's next synchronisation.

@@ -24,7 +24,7 @@
  * elements in all; the library allocates nothing).
  *
  * Types and sizes.  dtype FA_DTYPE_BF16 or FA_DTYPE_F16 (fa_fwd.h); d = 64 or
- * 128; B, H, N > 0; N * d * 2 below 2^31 bytes per head.
+ * 128; B, H, N > 0; N * d * 4 below 2^31 (as for fa_fwd).
  *
  * Errors (fa_status of fa_fwd.h).  Every check runs before any HIP call:
  * FA_ERR_INVALID for null pointers, s or p not 16-byte aligned, B, H, N or

@@ -140,6 +140,7 @@ def test_standard_argument_checks():
     assert std(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
     assert std(d=96) == fa.FA_ERR_UNSUPPORTED
     assert std(N=1 << 23, d=128) == fa.FA_ERR_UNSUPPORTED
+    assert std(N=1 << 22, d=128) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_per_dtype_entry_points_share_validation():
@@ -181,6 +182,7 @@ def test_backward_argument_checks():
     assert bwd(dtype=9) == fa.FA_ERR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERR_UNSUPPORTED
     assert bwd(N=1 << 23, d=128) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(N=1 << 22, d=128) == fa.FA_ERR_UNSUPPORTED      # N d 4 = 2^31: as for the forward
     # inputs may alias each other; with valid arguments the call only fails for lack of a GPU
     assert bwd(k=Q, v=Q) in (fa.FA_ERR_HIP, fa.FA_OK)
     for fn in (fa.fa_bwd_bf16, fa.fa_bwd_f16):

@@ -29,7 +29,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((uint64_t)N * d * 2 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    // per-head bytes, with room for the 32-bit row offsets of the padded
+    // last block (rows up to N + 255) as in the forward
+    if ((uint64_t)N * d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t heads = (uint64_t)B * H, nblk = ((uint64_t)N + 127) / 128;
     if (heads * nblk >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t tb = heads * N * d * 2, sb = heads * N * 4;

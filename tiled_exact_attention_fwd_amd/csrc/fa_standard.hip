@@ -231,7 +231,8 @@ extern "C" int fa_standard_fwd(const void* q, const void* k, const void* v, void
     if (!std::isfinite(scale)) return FA_ERR_INVALID;
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((uint64_t)N * d * 2 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+    // (room for the 32-bit row offsets of a padded last block, as in the forward)
+    if ((uint64_t)N * d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t blocks = (uint64_t)B * H * ((N + 3) / 4);
     if (blocks >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     int cus = 0;
