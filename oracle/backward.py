@@ -116,6 +116,8 @@ def attention_bwd_sampled(qh, kh, vh, doh, scale, causal, q_rows, k_rows, chunk=
 
     qh, kh, vh, doh : [N, d] arrays (widened to float64).
     Returns ``(dq [len(q_rows), d], dk [len(k_rows), d], dv [len(k_rows), d])``.
+    With no key rows asked for, only the requested query rows are visited
+    (a row's dQ needs only that row's P, dP and centring).
     """
     qh, kh, vh, doh = _as64(qh), _as64(kh), _as64(vh), _as64(doh)
     n, d = qh.shape
@@ -124,6 +126,15 @@ def attention_bwd_sampled(qh, kh, vh, doh, scale, causal, q_rows, k_rows, chunk=
     dq = np.zeros((len(q_rows), d))
     dk = np.zeros((len(k_rows), d))
     dv = np.zeros((len(k_rows), d))
+    if len(k_rows) == 0:
+        for i0 in range(0, len(q_rows), chunk):
+            rows = q_rows[i0:i0 + chunk]
+            s = np.where(_visible(rows, kh.shape[0], causal), _scores(qh[rows], kh, scale), -np.inf)
+            p, _ = _softmax_rows(s)
+            dp = doh[rows] @ vh.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[i0:i0 + len(rows)] = scale * (ds @ kh)
+        return dq, dk, dv
     for c0 in range(0, n, chunk):
         rows = np.arange(c0, min(c0 + chunk, n))
         s = np.where(_visible(rows, kh.shape[0], causal), _scores(qh[rows], kh, scale), -np.inf)

@@ -258,3 +258,33 @@ def test_zero_and_negative_scale(causal):
         else:
             errs = grad_errors(dev, ref, "bf16")
         assert max(errs.values()) <= TOL["bf16"], (scale, errs)
+
+
+def test_maximum_size():
+    """The largest head the library accepts at d = 128 (N d 4 < 2^31,
+    N = 4194303, ragged), causal bf16: every output finite, dQ at sampled
+    rows against the oracle (each row alone), and one more row rejected."""
+    import time
+    N, d = (1 << 22) - 1, 128
+    t0 = time.time()
+    print(f"backward maximum size: B=1 H=1 N={N} d={d} bf16 causal", flush=True)
+    words, dwords = inputs((1, 1, N, d), "bf16", "normal", 42)
+    print(f"  inputs drawn ({time.time() - t0:.0f} s)", flush=True)
+    (qd, kd, vd, dod, o, lse), (dq, dk, dv, delta) = run_device(words, dwords, "bf16", True, W.scale_for(d))
+    print(f"  forward and backward done ({time.time() - t0:.0f} s)", flush=True)
+    for t in (dq, dk, dv, delta):
+        assert bool(torch.isfinite(t).all())
+    st = fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), dod.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), 1, 1, N + 1, d,
+                   W.scale_for(d), 1, torch.cuda.current_stream().cuda_stream, fa.FA_DTYPE_BF16)
+    assert st == fa.FA_ERR_UNSUPPORTED
+    rng = np.random.default_rng(10)
+    # the first rows carry the largest dQ entries (the gate's scale), then
+    # tile edges and random rows
+    qr = np.unique(np.concatenate([np.arange(64), sample_rows(N, 256, rng, n_random=8)]))
+    vals = [W.decode64(w[0, 0], "bf16") for w in (*words, dwords)]
+    ref, _, _ = oracle.attention_bwd_sampled(*vals, W.scale_for(d), True, qr, [], chunk=64)
+    print(f"  oracle rows done ({time.time() - t0:.0f} s)", flush=True)
+    errs = grad_errors([out_to64(dq[0, 0, qr])], [ref], "bf16")
+    print(f"  {errs}", flush=True)
+    assert errs["dq"] <= TOL["bf16"], errs

@@ -190,3 +190,14 @@ def test_sampled_rows_equal_full(causal):
     np.testing.assert_allclose(dq, full[0][0, 0, qr], atol=1e-13, rtol=0)
     np.testing.assert_allclose(dk, full[1][0, 0, kr], atol=1e-13, rtol=0)
     np.testing.assert_allclose(dv, full[2][0, 0, kr], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_query_rows_only_equal_full(causal):
+    rng = np.random.default_rng(9)
+    q, k, v, do = rand4(rng, 1, 1, 41, 5)
+    full = obwd.attention_bwd_ref(q, k, v, do, 0.7, causal)
+    qr = np.array([40, 0, 17, 3])
+    dq, dk, dv = obwd.attention_bwd_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.7, causal, qr, [], chunk=3)
+    np.testing.assert_allclose(dq, full[0][0, 0, qr], atol=1e-13, rtol=0)
+    assert dk.shape == (0, 5) and dv.shape == (0, 5)

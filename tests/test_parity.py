@@ -397,3 +397,36 @@ def test_guard_bands_untouched():
         assert bool((obuf[:pad] == 7.0).all()) and bool((obuf[pad + n_o:] == 7.0).all())
         assert bool((lbuf[:pad] == -3.0).all()) and bool((lbuf[pad + n_l:] == -3.0).all())
         assert bool(torch.isfinite(o.float()).all())
+
+
+def test_maximum_size():
+    """The largest head the library accepts at d = 128 (N d 4 < 2^31:
+    N = 4194303, 1 GiB per tensor, a ragged last tile), causal bf16: sampled
+    rows -- the first, the last, both sides of tile boundaries, random ones --
+    against the oracle over all N keys."""
+    import time
+    N, d = (1 << 22) - 1, 128
+    t0 = time.time()
+    print(f"maximum size: B=1 H=1 N={N} d={d} bf16 causal", flush=True)
+    words = W.make_words((1, 1, N, d), "bf16", "normal", seed=41)
+    print(f"  inputs drawn ({time.time() - t0:.0f} s)", flush=True)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    scale = W.scale_for(d)
+    o, lse = fa.attention(qd, kd, vd, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    print(f"  forward done ({time.time() - t0:.0f} s)", flush=True)
+    # one more row would exceed the per-head limit
+    bigger = fa.fa_fwd_bf16(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), 1, 1, N + 1,
+                            d, scale, 1, torch.cuda.current_stream().cuda_stream)
+    assert bigger == fa.FA_ERR_UNSUPPORTED
+    rng = np.random.default_rng(9)
+    rows = sample_rows(N, 128, rng, n_random=8)
+    vals = [W.decode64(w[0, 0], "bf16")[None, None] for w in words]
+    o_ref, lse_ref = oracle.attention_ref(vals[0], vals[1], vals[2], scale, True, rows=rows)
+    print(f"  oracle rows done ({time.time() - t0:.0f} s)", flush=True)
+    o_np = out_to64(o[0, 0, rows])[None, None]
+    lse_np = lse[0, 0, rows].cpu().numpy().astype(np.float64)[None, None]
+    errs = gate_errors(None, o_np, lse_np, o_ref, lse_ref, "bf16")
+    print(f"  {errs}", flush=True)
+    assert_gates(errs, "bf16", "maximum size")
+    assert bool(torch.isfinite(lse).all())
