@@ -222,3 +222,24 @@ def test_split_ranges_rule():
             assert 1 <= len(r) <= s and r[0][0] == 0 and r[-1][1] == N
             assert all(a < b for a, b in r) and all(r[i][1] == r[i + 1][0] for i in range(len(r) - 1))
             assert all(a % 64 == 0 for a, _ in r)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The binding, its build script and the input generators import nothing
+    from oracle/ (only the tests, the smoke check and the bench's CPU
+    baseline may); checked in a fresh interpreter and in the sources."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; import tiled_exact_attention_fwd_amd as fa, fa_workloads; "
+            "import tiled_exact_attention_fwd_amd.build, tiled_exact_attention_fwd_amd.codeobj; fa.lib(); "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    pkg = os.path.join(root, "tiled_exact_attention_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import oracle|from oracle)", text, flags=re.M), f
