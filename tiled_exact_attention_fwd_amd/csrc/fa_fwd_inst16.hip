@@ -41,7 +41,9 @@ int FA_XCAT6(launch16s_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)(const FwdParam
                                      (hipStream_t)stream);
     if (err != hipSuccess) return FA_ERR_HIP;
     const int rows = p.heads * p.N;
-    hipLaunchKernelGGL((split_merge_kernel<FA_TYPE(FA_INST_T), FA_INST_D>), dim3((rows + 3) / 4), dim3(256), 0,
+    constexpr int rows_per_block = 256 / (FA_INST_D / 8);
+    hipLaunchKernelGGL((split_merge_kernel<FA_TYPE(FA_INST_T), FA_INST_D>),
+                       dim3((rows + rows_per_block - 1) / rows_per_block), dim3(256), 0,
                        (hipStream_t)stream, (const float*)p.o, (const float*)p.lse, o, lse, rows, p.splits);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

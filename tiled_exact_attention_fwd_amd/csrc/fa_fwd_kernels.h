@@ -858,33 +858,37 @@ struct Fwd16 {
 // ("Flash Attention 原理", Softmax 的分块计算; the correction factor of
 // "FlashAttention分块计算优化Transformer显存效率" §3.2): with
 // LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
-// One wave per row; a lane merges D / 64 consecutive columns.
+// A thread merges 8 consecutive columns of one row.
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ void __launch_bounds__(256) split_merge_kernel(const float* opart, const float* lpart, void* o,
                                                           float* lse, int rows, int splits) {
-    constexpr int CPL = D / 64;                     // columns per lane
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (row >= rows) return;                        // whole waves; no barrier follows
+    // a thread merges 8 consecutive columns of one row: D / 8 threads per
+    // row, 16-byte loads of the fp32 partials and one 16-byte store
+    constexpr int TPR = D / 8;                      // threads per row
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int row = t / TPR, c0 = (t % TPR) * 8;
+    if (row >= rows) return;                        // no barrier follows
     float m = -__builtin_inff();
     for (int s = 0; s < splits; ++s) m = fmaxf(m, lpart[(size_t)s * rows + row]);
     float den = 0.f;
     for (int s = 0; s < splits; ++s) den += expf(lpart[(size_t)s * rows + row] - m);
     const float total = m + logf(den);
-    float acc[CPL] = {};
+    float acc[8] = {};
     for (int s = 0; s < splits; ++s) {
         const float w = expf(lpart[(size_t)s * rows + row] - total);
-        const float* src = opart + ((size_t)s * rows + row) * D + lane * CPL;
+        const f32x4_t* src = (const f32x4_t*)(opart + ((size_t)s * rows + row) * D + c0);
+        const f32x4_t a = src[0], b = src[1];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) acc[e] += w * src[e];
+        for (int e = 0; e < 4; ++e) {
+            acc[e] += w * a[e];
+            acc[4 + e] += w * b[e];
+        }
     }
-    uint16_t* dst = (uint16_t*)o + (size_t)row * D + lane * CPL;
-    if constexpr (CPL == 2) {
-        *(__attribute__((address_space(1))) uint32_t*)dst = pack2<T>(acc[0], acc[1]);
-    } else {
-        *(__attribute__((address_space(1))) uint16_t*)dst = (uint16_t)(pack2<T>(acc[0], 0.f) & 0xffffu);
-    }
-    if (lane == 0) lse[row] = total;
+    gstore((uint16_t*)o + (size_t)row * D + c0,
+           u32x4_t{pack2<T>(acc[0], acc[1]), pack2<T>(acc[2], acc[3]), pack2<T>(acc[4], acc[5]),
+                   pack2<T>(acc[6], acc[7])});
+    if (c0 == 0) gstore(lse + row, total);
 }
 
 // ---------------------------------------------------------------------------
