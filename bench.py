@@ -28,6 +28,9 @@ registers, spills, LDS bytes and occupancy beside the working set of
 shape, non-causal and causal (after the copy kernel, for counter runs); the
 default line carries the same figures in its "backward" object.
 
+--configs times the forward (launch mean) and, for 16-bit inputs, the
+backward on every named workload, one JSON line each.
+
 --split times the split-KV forward (fa_fwd_split, 2-16 key ranges) against
 the plain launch on few-head long sequences (bf16, d = 128, non-causal and
 causal).
@@ -318,6 +321,30 @@ def split_kv(steps, warmup):
         del q, k, v, o, lse, op, lp
 
 
+def all_configs(steps, warmup):
+    """Every named workload (C1-C5, each mask setting): forward time and
+    TFLOP/s with its fraction of the matching dense MFMA peak, and for the
+    16-bit ones the backward's time and TFLOP/s (10 B H N^2 d, halved causal).
+    One JSON line per workload."""
+    import fa_workloads as W
+    for name, wl in W.WORKLOADS.items():
+        for causal in wl.causal:
+            r = time_workload(wl, causal, steps, warmup)
+            f = wl.flops(causal)
+            tf = f / (r["launch_mean_ms"] * 1e-3) / 1e12
+            row = {"workload": name, "shape": list(wl.shape), "dtype": wl.dtype, "values": wl.values,
+                   "causal": causal, "fwd_us": round(r["launch_mean_ms"] * 1e3, 1), "fwd_TFLOP/s": round(tf, 1),
+                   "fwd_frac": round(tf / PEAK_TFLOPS[wl.dtype], 4),
+                   "hbm_min_GB/s": round((4 * wl.B * wl.H * wl.N * wl.d * (4 if wl.dtype == "f32" else 2)
+                                          + 4 * wl.B * wl.H * wl.N) / (r["launch_mean_ms"] * 1e-3) / 1e9, 1)}
+            if wl.dtype != "f32":
+                ms = time_backward(wl, causal, max(5, steps // 4), max(3, warmup // 4))
+                bt = backward_flops(wl, causal) / (ms * 1e-3) / 1e12
+                row.update({"bwd_us": round(ms * 1e3, 1), "bwd_TFLOP/s": round(bt, 1),
+                            "bwd_frac": round(bt / PEAK_TFLOPS[wl.dtype], 4)})
+            print(json.dumps(row), flush=True)
+
+
 def cpu_baseline(seconds):
     """The float64 oracle on whole heads of the same workload, until about
     `seconds` of CPU work; returns the oracle's TFLOP/s equivalent."""
@@ -583,6 +610,7 @@ def main():
     ap.add_argument("--standard", action="store_true", help="time the standard (materialising) forward")
     ap.add_argument("--backward", action="store_true", help="time only the backward pass (fa_bwd)")
     ap.add_argument("--split", action="store_true", help="split-KV forward against the plain one, few heads")
+    ap.add_argument("--configs", action="store_true", help="forward and backward on every named workload")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
                          "'trace DIR [COUNT [SKIP]]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
@@ -613,6 +641,9 @@ def main():
         return
     if a.split:
         split_kv(a.steps, a.warmup)
+        return
+    if a.configs:
+        all_configs(a.steps, a.warmup)
         return
     if a.backward:
         copy_calibration()
