@@ -169,7 +169,8 @@ __device__ __forceinline__ void store_rows(uint16_t* out, int row, int N, const 
 }
 
 template <class T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3)))
+dq_kernel(BwdParams p) {
     using G = Geo<D>;
     // K and V tiles, double-buffered
     __shared__ __attribute__((aligned(16))) uint8_t ks[2][G::TILE * G::PITCH];
