@@ -167,6 +167,21 @@ int run(const fa_fwd_args* a) {
             return a->d == 64 ? fa::launch16p_bf16_d64(p, slots, a->stream) : fa::launch16p_bf16_d128(p, slots, a->stream);
         return a->d == 64 ? fa::launch16p_f16_d64(p, slots, a->stream) : fa::launch16p_f16_d128(p, slots, a->stream);
     }
+    // Under the causal mask at d = 128: the persistent kernel with 256-row
+    // query tiles (one workgroup per CU), each work unit a pair of query
+    // tiles (i, T - 1 - i) of one head, whose key tiles add up to the same
+    // count for every pair; the shortest tile must have 4 key tiles.
+    if (c && a->d == 128 && a->dtype != FA_DTYPE_F32 && !o32 && !count && slots > 0) {
+        const int tw = 256, tiles = (a->N + tw - 1) / tw;
+        const int nk_first = (std::min(tw, a->N) - 1) / tk + 1;
+        if (tiles % 2 == 0 && nk_first >= 4 && p.heads * tiles / 2 > slots) {
+            FwdParams pw = p;
+            pw.tiles_q = tiles;
+            pw.total = p.heads * tiles;
+            return a->dtype == FA_DTYPE_BF16 ? fa::launch16pcw_bf16_d128(pw, slots, a->stream)
+                                             : fa::launch16pcw_f16_d128(pw, slots, a->stream);
+        }
+    }
     // Likewise under the causal mask at d = 64, where two workgroups per CU
     // fit their K, V, Q and output staging in LDS: each takes pairs of query
     // tiles (i, T - 1 - i) of equal total cost, so T must be even.  Only for

@@ -56,7 +56,14 @@ int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid,
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>::BQ == tile_q16(false), "grid tile");
     return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>>(p, stream, grid);
 }
-#elif FA_INST_D == 64
+#elif FA_INST_D == 128
+// the causal persistent kernel with 256-row query tiles (d = 128, 16-bit
+// output, no counters)
+int FA_XCAT4(launch16pcw_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
+    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>::BQ == 256, "grid tile");
+    return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid);
+}
+#else
 // the causal persistent kernel (d = 64, 16-bit output, no counters)
 int FA_XCAT4(launch16pc_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>::BQ == tile_q16(true), "grid tile");

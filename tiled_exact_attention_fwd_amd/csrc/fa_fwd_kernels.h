@@ -924,9 +924,14 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* opart, co
 // at j = 0, so that tiles of two key tiles (j = 0 and j = nk - 1 = 1) work;
 // the diagonal's masks fall on the last two key tiles of a query tile.
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL = false>
+// WIDE: the causal kernel with eight waves (256-row query tiles, one
+// workgroup per CU, d = 128): every query tile then has at least four key
+// tiles, so it uses the transitions of the kernel without a mask (no
+// separate output slice), and the diagonal's masks fall on the last four key
+// tiles of a query tile.
+template <class T, int D, bool CAUSAL = false, bool WIDE = false>
 struct Fwd16P {
-    using Bs = Fwd16<T, D, CAUSAL, false, false>;
+    using Bs = Fwd16<T, D, CAUSAL, false, false, WIDE ? 8 : 0>;
     static constexpr int WAVES = Bs::WAVES, BQ = Bs::BQ, OCC = Bs::OCC, NT = Bs::NT, BK = Bs::BK;
     static constexpr int RESIDENT = Bs::RESIDENT;
     static constexpr int ROWB = Bs::ROWB, TILEB = Bs::TILEB, NS = Bs::NS, NDB = Bs::NDB, NMB = Bs::NMB;
@@ -935,15 +940,20 @@ struct Fwd16P {
     static constexpr bool READ_FIRST = Bs::READ_FIRST;
     static constexpr int SLICE = 32 * ROWB;          // one wave's Q / O staging bytes
     static constexpr int QLOADS = SLICE / 1024;      // 16-byte copies per lane of a wave's Q rows
-    static constexpr bool SPLIT = CAUSAL;            // the output has its own staging slice
+    static constexpr bool SPLIT = CAUSAL && !WIDE;   // the output has its own staging slice
     static constexpr int MIN_KEY_TILES = SPLIT ? 2 : 4;
     static constexpr int QCOPY_AT = SPLIT ? 0 : 2;   // key tile at which the next Q rows are copied
-    static constexpr int STEADY_LO = SPLIT ? 2 : 3;  // plain iterations: STEADY_LO <= j <= nk - 3
+    static constexpr int STEADY_LO = SPLIT ? 2 : 3;  // plain iterations: STEADY_LO <= j <= nk - 1 - TAIL
+    // key tiles at the end of a query tile that are never plain: the K copy
+    // of j + 2 crosses into the next tile from j = nk - 2 on, and under the
+    // mask the diagonal covers the last BQ / BK key tiles
+    static constexpr int TAIL = CAUSAL && BQ / BK > 2 ? BQ / BK : 2;
     static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
     static constexpr int RPS = 64 / CPR;             // rows per 16-byte store
-    static_assert(SLICE % 1024 == 0 && RESIDENT == (CAUSAL ? 2 : 1), "persistent shape");
+    static_assert(SLICE % 1024 == 0 && RESIDENT == (SPLIT ? 2 : 1), "persistent shape");
+    static_assert(!WIDE || (CAUSAL && Bs::WAVES == 8), "wide causal shape");
     static_assert((4 * TILEB + (SPLIT ? 2 : 1) * WAVES * SLICE) * RESIDENT <= 160 * 1024, "LDS per CU");
-    static_assert(!CAUSAL || BQ == 2 * BK, "causal masks on the last two key tiles");
+    static_assert(!SPLIT || BQ == 2 * BK, "causal masks on the last two key tiles");
 
     // The lane index, opaque to the optimiser: addresses derived from it in a
     // once-per-tile block are computed there, not hoisted out of the key loop
@@ -1119,10 +1129,14 @@ struct Fwd16P {
         // position of the softmax stream: key tile j0 of this workgroup's
         // query tile k0 (j0 = -1 before the first; j0 = nk until the wrap)
         int k0 = 0, j0 = -1;
-        // iterations with STEADY_LO <= j0 <= nk - 3 are plain: one range
-        // check, the copy sources advance by a tile; every other one
-        // recomputes its state in one block
-        auto steady_count = [&](int nkt) { return nkt > STEADY_LO + 2 ? (uint32_t)(nkt - STEADY_LO - 2) : 0u; };
+        // iterations with STEADY_LO <= j0 <= nk - 1 - TAIL are plain: one
+        // range check, the copy sources advance by a tile; every other one
+        // recomputes its state in one block (and applies the masks, so the
+        // last TAIL key tiles -- the K copy crossing into the next tile, and
+        // under the mask the diagonal's tiles -- are never plain)
+        auto steady_count = [&](int nkt) {
+            return nkt > STEADY_LO + TAIL ? (uint32_t)(nkt - STEADY_LO - TAIL) : 0u;
+        };
         uint32_t nk_s = steady_count(cur.nk);
         const uint8_t* kc_ptr = kptr;      // K copy of this iteration (key tile g + 2)
         const uint8_t* vc_ptr = vptr;      // V copy (key tile g)

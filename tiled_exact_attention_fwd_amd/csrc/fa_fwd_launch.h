@@ -42,6 +42,10 @@ constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TIL
 // causal persistent kernels (d = 64; an even number of query tiles, paired)
 int launch16pc_bf16_d64(const FwdParams& p, int grid, void* stream);
 int launch16pc_f16_d64(const FwdParams& p, int grid, void* stream);
+// causal persistent kernels with 256-row query tiles (d = 128; an even number
+// of query tiles, paired; every query tile at least 4 key tiles)
+int launch16pcw_bf16_d128(const FwdParams& p, int grid, void* stream);
+int launch16pcw_f16_d128(const FwdParams& p, int grid, void* stream);
 // split-KV launches: p.o / p.lse point at the fp32 partials ([p.splits,
 // B H, N] x d and [p.splits, B H, N]); the merge writes o and lse
 #define FA_DECLARE16S(T, D, C) \
