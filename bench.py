@@ -61,7 +61,7 @@ KERNEL_SOURCES = ("tiled_exact_attention_fwd_amd/csrc/fa_fwd_kernels.h",
                   "tiled_exact_attention_fwd_amd/csrc/fa_fwd_inst32.hip",
                   "tiled_exact_attention_fwd_amd/csrc/fa_fwd.hip")
 # the instance bench.py times for the headline (bf16, d=128, non-causal)
-HEADLINE_KERNEL = "fa::Fwd16P<fa::BF16, 128, false>"
+HEADLINE_KERNEL = "fa::Fwd16P<fa::BF16, 128, false, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_n4096_counters.txt")
 
 

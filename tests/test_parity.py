@@ -268,11 +268,16 @@ def test_causal_tile_order_covers_every_tile(B, H, N, d):
     ("f16", 1, 600, 512, 64, -0.4, True),      # causal: 4 query tiles per head, negative scale
     ("bf16", 4, 50, 700, 64, None, True),      # causal: 6 query tiles, ragged last tile (rows and keys)
     ("bf16", 1, 520, 256, 64, None, True),     # causal: one pair per head, tiles of 2 and 4 key tiles
+    # causal at d = 128: 256-row query tiles in pairs (the diagonal over the last 4 key tiles)
+    ("bf16", 4, 32, 2000, 128, None, True),    # 8 tiles per head, ragged last tile (208 rows), 512 pairs
+    ("f16", 2, 160, 1024, 128, -0.3, True),    # 4 tiles per head (4 .. 16 key tiles), negative scale
+    ("bf16", 1, 260, 512, 128, None, True),    # one pair per head: tiles of 4 and 8 key tiles
 ])
 def test_persistent_kernel(dtype, B, H, N, d, scale, causal):
     """Plain launches with more query tiles than the device has workgroup
     slots run the persistent kernel (without a mask; causal at d = 64 with
-    an even number of query tiles), which pipelines across query tiles; it
+    an even number of query tiles; causal at d = 128 with an even number of
+    256-row query tiles), which pipelines across query tiles; it
     matches the oracle on every head, gives the same bits as the per-tile
     kernel (the counters launch in launch_all), and repeats bit for bit."""
     words = W.make_words((B, H, N, d), dtype, "normal", seed=21)
