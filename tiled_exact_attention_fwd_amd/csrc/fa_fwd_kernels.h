@@ -40,7 +40,10 @@
 //   * Without a mask, launches with more query tiles than workgroup slots
 //     run a persistent variant (Fwd16P): one workgroup per CU runs the key
 //     loops of its query tiles back to back as one software pipeline, so the
-//     pipeline does not drain and refill between query tiles.
+//     pipeline does not drain and refill between query tiles.  Under the
+//     mask the persistent variant takes pairs of query tiles (i, T - 1 - i)
+//     of equal total cost: with 256-row tiles at d = 128, with 128-row tiles
+//     (two workgroups per CU) at d = 64.
 #pragma once
 
 #include <hip/hip_runtime.h>
