@@ -21,7 +21,9 @@
  * gradient dO.
  *
  * Entry points (one per element type, plus a generic form with a trailing
- * dtype as in fa_fwd.h):
+ * dtype as in fa_fwd.h).  bf16 and fp16 run the 16-bit matrix-core products
+ * with P and dS rounded to the input type and fp32 accumulation; fp32 runs
+ * fp32 matrix-core products throughout and writes fp32 gradients.
  *
  *   q, k, v, o, dout : device, const, dense row-major [B, H, N, d] of the
  *                      element type; o and lse are the forward's outputs for
@@ -42,7 +44,7 @@
  * Errors (fa_status of fa_fwd.h); every check runs before any HIP call:
  * FA_ERR_INVALID for a null pointer, B, H, N or d <= 0, causal not 0 or 1, a
  * non-finite scale, or an output overlapping an input or another output;
- * FA_ERR_UNSUPPORTED for fp32 (no backward kernel is built for it), d other
+ * FA_ERR_UNSUPPORTED for another element type, d other
  * than 64 or 128, N * d * 4 of 2^31 or more (as for fa_fwd), a grid beyond 2^31
  * workgroups, or a current device that is not gfx950; FA_ERR_HIP if the
  * device query or a launch fails.  Faults inside a kernel surface
@@ -59,6 +61,9 @@ int fa_bwd_bf16(const void* q, const void* k, const void* v, const void* o, cons
                 void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
                 void* stream);
 int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream);
+int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
                void* stream);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,

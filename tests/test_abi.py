@@ -178,14 +178,15 @@ def test_backward_argument_checks():
     assert bwd(dq=Q + nbytes - 2) == fa.FA_ERR_INVALID            # output over an input
     assert bwd(dv=DK + 64) == fa.FA_ERR_INVALID                   # outputs overlap each other
     assert bwd(delta=L + 4) == fa.FA_ERR_INVALID                  # work array over the lse input
-    assert bwd(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(dtype=fa.FA_DTYPE_F32) in (fa.FA_ERR_HIP, fa.FA_OK)            # fp32 is built
+    assert bwd(dtype=fa.FA_DTYPE_F32, dq=Q + 2 * 3 * 100 * 64 * 4 - 4) == fa.FA_ERR_INVALID   # 4-byte elements
     assert bwd(dtype=9) == fa.FA_ERR_UNSUPPORTED
     assert bwd(d=96) == fa.FA_ERR_UNSUPPORTED
     assert bwd(N=1 << 23, d=128) == fa.FA_ERR_UNSUPPORTED
     assert bwd(N=1 << 22, d=128) == fa.FA_ERR_UNSUPPORTED      # N d 4 = 2^31: as for the forward
     # inputs may alias each other; with valid arguments the call only fails for lack of a GPU
     assert bwd(k=Q, v=Q) in (fa.FA_ERR_HIP, fa.FA_OK)
-    for fn in (fa.fa_bwd_bf16, fa.fa_bwd_f16):
+    for fn in (fa.fa_bwd_bf16, fa.fa_bwd_f16, fa.fa_bwd_f32):
         assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 0, 1, 1, 64, 1.0, 0, None) == fa.FA_ERR_INVALID
         assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 1, 1, 48, 1.0, 0, None) == fa.FA_ERR_UNSUPPORTED
 

@@ -8,9 +8,9 @@ The oracle computes the exact gradients from Q, K, V and dO alone; nothing it
 uses comes from the device.
 
 Gate.  No tolerance is stated for gradients, and gradients have no fixed
-scale, so the forward's output tolerances (1e-2 for bf16, 2e-3 for fp16,
-applied there to outputs of order one) are applied relative to the largest
-reference entry of each gradient:
+scale, so the forward's output tolerances (1e-2 for bf16, 2e-3 for fp16 and
+fp32, applied there to outputs of order one) are applied relative to the
+largest reference entry of each gradient:
 max(|g - g_ref| - half_ulp(g_ref)) <= tol * max|g_ref|, the half ulp being
 the rounding of the 16-bit output itself.  A CPU emulation of the kernels'
 arithmetic (P and dS rounded to the input type before their products, fp32
@@ -29,7 +29,7 @@ from parity_util import half_ulp, out_to64, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 1e-2, "f16": 2e-3}
+TOL = {"bf16": 1e-2, "f16": 2e-3, "f32": 2e-3}
 
 
 def inputs(shape, dtype, values, seed):
@@ -72,7 +72,7 @@ def check(words, dwords, dtype, causal, scale, heads=None, what=""):
     return errs, (dq, dk, dv, delta)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 33, 200, 257])
@@ -81,6 +81,9 @@ def test_small(dtype, d, causal, N):
     words, dwords = inputs((1, 2, N, d), dtype, "normal", 3)
     errs, _ = check(words, dwords, dtype, causal, W.scale_for(d), what="small")
     print(errs)
+    if dtype == "f32":
+        # fp32 products throughout (no 16-bit P or dS): far inside the gate
+        assert max(errs.values()) <= 1e-4, errs
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -288,3 +291,14 @@ def test_maximum_size():
     errs = grad_errors([out_to64(dq[0, 0, qr])], [ref], "bf16")
     print(f"  {errs}", flush=True)
     assert errs["dq"] <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_configuration(causal):
+    """The fp32 configuration (B=1, H=1, N=256, d=64, N(0,1)) forward and
+    backward against the oracle, and a ragged multi-head fp32 case."""
+    for shape in ((1, 1, 256, 64), (2, 3, 300, 128)):
+        words, dwords = inputs(shape, "f32", "normal", 15)
+        errs, _ = check(words, dwords, "f32", causal, W.scale_for(shape[3]), what="f32")
+        print("f32", shape, causal, errs)
+        assert max(errs.values()) <= 1e-4, errs

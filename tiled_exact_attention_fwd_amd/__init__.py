@@ -5,7 +5,7 @@ The functions named like the C entry points (``fa_fwd_bf16``, ``fa_fwd_f16``,
 ``fa_fwd_f32``, ``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_split``, ``fa_fwd_tile_shape``,
 ``fa_strerror``, ``fa_build_info``, ``fa_standard_fwd`` of
 ``include/fa_standard.h``, the materialising baseline, and ``fa_bwd_bf16``,
-``fa_bwd_f16``, ``fa_bwd`` of ``include/fa_bwd.h``, the backward with
+``fa_bwd_f16``, ``fa_bwd_f32``, ``fa_bwd`` of ``include/fa_bwd.h``, the backward with
 recomputation) only marshal arguments: pointers are
 plain integers (device addresses), the stream an integer ``hipStream_t``
 handle, and the C status code is returned unchanged.
@@ -57,6 +57,7 @@ SIGNATURES = {
     "fa_fwd_split": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _I, _P, _I]),
     "fa_bwd_bf16": (_I, _BWD17),
     "fa_bwd_f16": (_I, _BWD17),
+    "fa_bwd_f32": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
 }
 
@@ -196,6 +197,10 @@ def fa_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, caus
     return lib().fa_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
 
 
+def fa_bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream):
+    return lib().fa_bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+
+
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype):
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype)
 
@@ -203,8 +208,8 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, 
 def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
     """Gradients ``(dq, dk, dv)`` of the attention forward on the device
     (include/fa_bwd.h), from the forward's ``o`` and ``lse`` for the same
-    inputs and the output gradient ``dout`` (16-bit [B, H, N, d] tensors,
-    lse [B, H, N] fp32).  Also returns the ``delta`` work array the call
+    inputs and the output gradient ``dout`` ([B, H, N, d] tensors of one
+    type, bf16, fp16 or fp32; lse [B, H, N] fp32).  Also returns the ``delta`` work array the call
     wrote (rowsum(dout * o), fp32)."""
     import math
     import torch

@@ -41,6 +41,7 @@ for c in (0, 1):
     UNITS.append((f"inst32_c{c}", "fa_fwd_inst32.hip", [f"-DFA_INST_C={c}"]))
 # backward kernels, one unit per element type and head dimension
 UNITS.append(("fa_bwd", "fa_bwd.hip", []))
+UNITS.append(("bwd_f32", "fa_bwd_inst32.hip", []))
 for t in ("bf16", "f16"):
     for d in (64, 128):
         UNITS.append((f"bwd_{t}_d{d}", "fa_bwd_inst.hip", [f"-DFA_INST_T={t}", f"-DFA_INST_D={d}"]))

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "fa_bwd.h"
+#include "fa_bwd32_kernels.h"
 #include "fa_bwd_kernels.h"
 #include "fa_bwd_launch.h"
 #include "fa_fwd.h"
@@ -26,15 +27,15 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID;
     if (!std::isfinite(scale)) return FA_ERR_INVALID;
-    if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    const uint64_t e = dtype == FA_DTYPE_F32 ? 4 : 2;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     // per-head bytes, with room for the 32-bit row offsets of the padded
     // last block (rows up to N + 255) as in the forward
     if ((uint64_t)N * d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t heads = (uint64_t)B * H, nblk = ((uint64_t)N + 127) / 128;
     if (heads * nblk >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
-    const uint64_t tb = heads * N * d * 2, sb = heads * N * 4;
+    const uint64_t tb = heads * N * d * e, sb = heads * N * 4;
     const void* ins[6] = {q, k, v, o, dout, lse};
     const uint64_t inb[6] = {tb, tb, tb, tb, tb, sb};
     void* outs[4] = {dq, dk, dv, delta};
@@ -48,6 +49,17 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     int cus = 0;
     const int dev_st = fa::device_check(&cus);
     if (dev_st != FA_OK) return dev_st;
+    if (dtype == FA_DTYPE_F32) {
+        fa::bwd::BwdParams32 p32;
+        p32.q = (const float*)q; p32.k = (const float*)k; p32.v = (const float*)v;
+        p32.o = (const float*)o; p32.dout = (const float*)dout; p32.lse = lse;
+        p32.dq = (float*)dq; p32.dk = (float*)dk; p32.dv = (float*)dv; p32.delta = delta;
+        p32.N = N;
+        p32.nblk = (int)nblk;
+        p32.c = scale * fa::bwd::kLog2e;
+        p32.scale = scale;
+        return fa::bwd::launch_bwd_f32(p32, (int)heads, d, causal != 0, stream) == 0 ? FA_OK : FA_ERR_HIP;
+    }
     fa::bwd::BwdParams p;
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
     p.o = (const uint16_t*)o; p.dout = (const uint16_t*)dout; p.lse = lse;
@@ -88,6 +100,12 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
                void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
                void* stream) {
     return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, FA_DTYPE_F16);
+}
+
+int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, FA_DTYPE_F32);
 }
 
 }  // extern "C"

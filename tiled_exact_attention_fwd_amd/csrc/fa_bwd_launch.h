@@ -6,11 +6,14 @@ namespace fa {
 namespace bwd {
 
 struct BwdParams;
+struct BwdParams32;
 
 int launch_bwd_bf16_d64(const BwdParams& p, int heads, bool causal, void* stream);
 int launch_bwd_bf16_d128(const BwdParams& p, int heads, bool causal, void* stream);
 int launch_bwd_f16_d64(const BwdParams& p, int heads, bool causal, void* stream);
 int launch_bwd_f16_d128(const BwdParams& p, int heads, bool causal, void* stream);
+// fp32, d = 64 or 128
+int launch_bwd_f32(const BwdParams32& p, int heads, int d, bool causal, void* stream);
 
 }  // namespace bwd
 }  // namespace fa
