@@ -323,9 +323,9 @@ def split_kv(steps, warmup):
 
 def all_configs(steps, warmup):
     """Every named workload (C1-C5, each mask setting): forward time and
-    TFLOP/s with its fraction of the matching dense MFMA peak, and for the
-    16-bit ones the backward's time and TFLOP/s (10 B H N^2 d, halved causal).
-    One JSON line per workload."""
+    TFLOP/s with its fraction of the matching dense MFMA peak, and the
+    backward's time and TFLOP/s (10 B H N^2 d, halved causal).  One JSON line
+    per workload."""
     import fa_workloads as W
     for name, wl in W.WORKLOADS.items():
         for causal in wl.causal:
@@ -337,11 +337,10 @@ def all_configs(steps, warmup):
                    "fwd_frac": round(tf / PEAK_TFLOPS[wl.dtype], 4),
                    "hbm_min_GB/s": round((4 * wl.B * wl.H * wl.N * wl.d * (4 if wl.dtype == "f32" else 2)
                                           + 4 * wl.B * wl.H * wl.N) / (r["launch_mean_ms"] * 1e-3) / 1e9, 1)}
-            if wl.dtype != "f32":
-                ms = time_backward(wl, causal, max(5, steps // 4), max(3, warmup // 4))
-                bt = backward_flops(wl, causal) / (ms * 1e-3) / 1e12
-                row.update({"bwd_us": round(ms * 1e3, 1), "bwd_TFLOP/s": round(bt, 1),
-                            "bwd_frac": round(bt / PEAK_TFLOPS[wl.dtype], 4)})
+            ms = time_backward(wl, causal, max(5, steps // 4), max(3, warmup // 4))
+            bt = backward_flops(wl, causal) / (ms * 1e-3) / 1e12
+            row.update({"bwd_us": round(ms * 1e3, 1), "bwd_TFLOP/s": round(bt, 1),
+                        "bwd_frac": round(bt / PEAK_TFLOPS[wl.dtype], 4)})
             print(json.dumps(row), flush=True)
 
 
