@@ -143,7 +143,7 @@ typedef struct {
 int fa_fwd_ex(const fa_fwd_args* args);
 
 /*
- * Split-KV forward (16-bit inputs): the keys of every head are cut into
+ * Split-KV forward: the keys of every head are cut into
  * `splits` ranges of whole 64-key tiles (fewer when N has fewer key tiles),
  * each (query tile, key range) runs as its own workgroup and writes the
  * partial output and log-sum-exp of its range's softmax in fp32, and a
@@ -160,10 +160,11 @@ int fa_fwd_ex(const fa_fwd_args* args);
  *   lse_part   device work array of splits * B * H * N fp32
  *   causal     as for fa_fwd
  *   splits     key ranges requested, >= 1
- *   dtype      FA_DTYPE_BF16 or FA_DTYPE_F16
+ *   dtype      FA_DTYPE_BF16, FA_DTYPE_F16 or FA_DTYPE_F32 (fp32: 64-row query
+ *              tiles on the fp32 matrix cores, fp32 output)
  * The caller allocates the work arrays; they must not overlap any input,
- * output or each other (FA_ERR_INVALID), nor may splits be < 1.  fp32 inputs
- * are FA_ERR_UNSUPPORTED; other checks as for fa_fwd.
+ * output or each other (FA_ERR_INVALID), nor may splits be < 1; other checks
+ * as for fa_fwd.
  */
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                  float* o_part, float* lse_part, int B, int H, int N, int d,

@@ -208,7 +208,8 @@ def test_split_argument_checks():
     assert split(lse_part=O + 16) == fa.FA_ERR_INVALID        # work array over the output
     assert split(lse_part=OP + 1024) == fa.FA_ERR_INVALID     # the two work arrays overlap
     assert split(scale=float("nan")) == fa.FA_ERR_INVALID
-    assert split(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert split(dtype=fa.FA_DTYPE_F32) in (fa.FA_ERR_HIP, fa.FA_OK)      # fp32 is built
+    assert split(dtype=fa.FA_DTYPE_F32, o_part=Q + 2 * 3 * 100 * 64 * 4 - 4) == fa.FA_ERR_INVALID
     assert split(d=80) == fa.FA_ERR_UNSUPPORTED
     assert split(causal=2) == fa.FA_ERR_INVALID
     assert split() in (fa.FA_ERR_HIP, fa.FA_ERR_UNSUPPORTED, fa.FA_OK)   # valid: fails only for lack of a GPU

@@ -32,7 +32,7 @@ def run(shape, dtype, splits, values="normal", seed=11, scale=None, causal=False
     return words, (qd, kd, vd), (o, lse, op, lp), scale
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,splits", [(1, 3), (200, 2), (1000, 3), (1000, 7), (4100, 5)])
@@ -66,7 +66,7 @@ def test_split_matches_oracle(dtype, d, causal, N, splits):
             assert e1 <= TOL_O[dtype] and el <= TOL_LSE, (s, k0, k1, e1, el)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_one_range_equals_plain_forward(dtype, d, causal):
@@ -74,7 +74,8 @@ def test_one_range_equals_plain_forward(dtype, d, causal):
     words, (qd, kd, vd), (o, lse, _, _), scale = run(shape, dtype, 1, causal=causal)
     o_ref, lse_ref = fa.attention(qd, kd, vd, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(o.view(bits), o_ref.view(bits))
     assert torch.equal(lse, lse_ref)
 
 

@@ -216,9 +216,9 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
     if (st != FA_OK) return st;
     if (!o_part || !lse_part || splits < 1) return FA_ERR_INVALID;
     if (a->out_dtype || a->counters || a->tile_q || a->tile_k) return FA_ERR_UNSUPPORTED;
-    if (a->dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     const bool causal = a->causal != 0;
-    const int tq = fa::tile_q16(causal), tk = 64;
+    const bool f32 = a->dtype == FA_DTYPE_F32;
+    const int tq = f32 ? 64 : fa::tile_q16(causal), tk = 64;
     // ranges of whole key tiles; as many as asked for, at most one per key tile
     const int nk = (a->N + tk - 1) / tk;
     const int per = (nk + std::min(splits, nk) - 1) / std::min(splits, nk);   // key tiles per range
@@ -248,11 +248,14 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
     p.total = (int)tiles;
     p.group = 1;
     p.c = std::fmax(std::fabs(a->scale) * 1.4426950408889634f, FLT_MIN);
-    p.qsign = a->scale < 0.f ? 0x80008000u : 0u;
+    p.qsign = a->scale < 0.f ? (f32 ? 0x80000000u : 0x80008000u) : 0u;
     p.counters = nullptr;
     p.splits = used;
     p.split_len = per * tk;
     const bool bf = a->dtype == FA_DTYPE_BF16, d64 = a->d == 64;
+    if (f32)
+        return causal ? fa::launch32s_c1(p, a->d, a->o, a->lse, a->stream)
+                      : fa::launch32s_c0(p, a->d, a->o, a->lse, a->stream);
     if (causal)
         return bf ? (d64 ? fa::launch16s_bf16_d64_c1(p, a->o, a->lse, a->stream)
                          : fa::launch16s_bf16_d128_c1(p, a->o, a->lse, a->stream))

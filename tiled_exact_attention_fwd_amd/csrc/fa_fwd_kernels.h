@@ -888,9 +888,14 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* opart, co
             acc[4 + e] += w * b[e];
         }
     }
-    gstore((uint16_t*)o + (size_t)row * D + c0,
-           u32x4_t{pack2<T>(acc[0], acc[1]), pack2<T>(acc[2], acc[3]), pack2<T>(acc[4], acc[5]),
-                   pack2<T>(acc[6], acc[7])});
+    if constexpr (__is_same(T, float)) {   // fp32 output
+        gstore((float*)o + (size_t)row * D + c0, f32x4_t{acc[0], acc[1], acc[2], acc[3]});
+        gstore((float*)o + (size_t)row * D + c0 + 4, f32x4_t{acc[4], acc[5], acc[6], acc[7]});
+    } else {
+        gstore((uint16_t*)o + (size_t)row * D + c0,
+               u32x4_t{pack2<T>(acc[0], acc[1]), pack2<T>(acc[2], acc[3]), pack2<T>(acc[4], acc[5]),
+                       pack2<T>(acc[6], acc[7])});
+    }
     if (c0 == 0) gstore(lse + row, total);
 }
 
@@ -1296,7 +1301,11 @@ struct Fwd16P {
 // fp32 kernel: fp32 MFMA (v_mfma_f32_32x32x2_f32), 64 x 64 tiles
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL, bool COUNT>
+// SPLIT: a split-KV launch (see Fwd16): one query tile over one range of
+// p.split_len keys, the range's partial output and log-sum-exp written to
+// range `split` of the fp32 work arrays; a row that sees no key of its range
+// leaves O = 0, LSE = -inf.
+template <int D, bool CAUSAL, bool COUNT, bool SPLIT = false>
 struct Fwd32 {
     static constexpr int BQ = 64;                  // 2 waves x 32 query rows
     static constexpr int WAVES = 2;
@@ -1323,7 +1332,25 @@ struct Fwd32 {
         const int li = lane & 31, lh = lane >> 5;
         const int N = p.N;
 
-        const TileId t = tile_of<CAUSAL>(blockIdx.x, p);
+        TileId t;
+        int split = 0;
+        if constexpr (SPLIT && CAUSAL) {
+            // (query tile, head, range), longest tiles first across the XCDs
+            const int per_rank = p.heads * p.splits;
+            const int rank = blockIdx.x / per_rank, rem = blockIdx.x - rank * per_rank;
+            t.qi = p.tiles_q - 1 - rank;
+            t.hh = rem / p.splits;
+            split = rem - t.hh * p.splits;
+        } else if constexpr (SPLIT) {
+            const int L = xcd_remap(blockIdx.x, p.total * p.splits);
+            const int per_head = p.tiles_q * p.splits;
+            t.hh = L / per_head;
+            const int rem = L - t.hh * per_head;
+            t.qi = rem / p.splits;
+            split = rem - t.qi * p.splits;
+        } else {
+            t = tile_of<CAUSAL>(blockIdx.x, p);
+        }
         const int hh = t.hh;
         const int qt0 = t.qi * BQ;
         const int q0w = qt0 + wave * 32;
@@ -1332,8 +1359,12 @@ struct Fwd32 {
         const size_t head_elems = (size_t)hh * N * D;
         const uint32_t head_bytes = (uint32_t)N * D * 4;
         const auto rq = make_rsrc((const uint8_t*)p.q + head_elems * 4, head_bytes);
-        const auto rk = make_rsrc((const uint8_t*)p.k + head_elems * 4, head_bytes);
-        const auto rv = make_rsrc((const uint8_t*)p.v + head_elems * 4, head_bytes);
+        // the keys this workgroup visits: the head's, or one range of them
+        const int kfirst = SPLIT ? split * p.split_len : 0;
+        const int NK = SPLIT ? min(p.split_len, N - kfirst) : N;
+        const uint32_t kv_bytes = (uint32_t)NK * D * 4;
+        const auto rk = make_rsrc((const uint8_t*)p.k + (head_elems + (size_t)kfirst * D) * 4, kv_bytes);
+        const auto rv = make_rsrc((const uint8_t*)p.v + (head_elems + (size_t)kfirst * D) * 4, kv_bytes);
 
         // Q^T operand for k-step s: Q[qrow][2 s + lh]
         float qreg[D / 2];
@@ -1349,8 +1380,14 @@ struct Fwd32 {
             qreg[4 * s4 + 3] = __uint_as_float((lh ? hi[3] : hi[2]) ^ sgn);
         }
 
-        const int nk = (N + BK - 1) / BK;
-        const int jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        const int nk = (NK + BK - 1) / BK;
+        int jend;
+        if constexpr (SPLIT && CAUSAL) {
+            const int kmax = min(qt0 + BQ, N) - 1 - kfirst;
+            jend = kmax < 0 ? 0 : min(nk, kmax / BK + 1);
+        } else {
+            jend = CAUSAL ? (min(qt0 + BQ, N) - 1) / BK + 1 : nk;
+        }
 
         f32x16_t acc[NDB];
 #pragma unroll
@@ -1367,7 +1404,7 @@ struct Fwd32 {
                 *(u32x4_t*)(vs + row * PITCH + 4 * c4) = buf_load16(rv, off);
             }
             __syncthreads();
-            const bool active = (!CAUSAL || k0 <= q0w + 31) && q0w < N;
+            const bool active = (!CAUSAL || kfirst + k0 <= q0w + 31) && q0w < N;
             if (active) {
                 f32x16_t s[NMB];
 #pragma unroll
@@ -1378,14 +1415,14 @@ struct Fwd32 {
                     for (int st = 0; st < D / 2; ++st)
                         s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(rp[2 * st], qreg[st], s[mb], 0, 0, 0);
                 }
-                const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+                const bool need_mask = (CAUSAL && kfirst + k0 + BK - 1 > q0w) || (k0 + BK > NK);
                 if (need_mask) {
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * lh + (r & 7);
-                            if ((CAUSAL && key > qrow) || key >= N) s[mb][r] = -__builtin_inff();
+                            if ((CAUSAL && kfirst + key > qrow) || key >= NK) s[mb][r] = -__builtin_inff();
                         }
                 }
                 float mx = -__builtin_inff();
@@ -1395,8 +1432,14 @@ struct Fwd32 {
                     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[mb][r]);
                 mx = max_halves(mx);
                 const float mnew = __builtin_fmaxf(m, mx);
-                const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
-                const float mc = mnew * c;
+                float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
+                float mc = mnew * c;
+                if constexpr (SPLIT) {
+                    // a row with no visible key so far: correction 1, terms 0
+                    const bool none = mnew == -__builtin_inff();
+                    alpha = none ? 1.0f : alpha;
+                    mc = none ? 0.f : mc;
+                }
                 m = mnew;
                 float ls = 0.f;
 #pragma unroll
@@ -1425,9 +1468,11 @@ struct Fwd32 {
         }
 
         const float lt = sum_halves(l);
+        // a split-KV launch writes range `split` of a [splits, B H, N] array
+        const size_t out_head = SPLIT ? ((size_t)split * p.heads + hh) * N : (size_t)hh * N;
         if (q0w < N && qrow < N) {
-            const float inv = 1.0f / lt;
-            const size_t orow = head_elems + (size_t)qrow * D;
+            const float inv = SPLIT ? (lt > 0.f ? 1.0f / lt : 0.f) : 1.0f / lt;
+            const size_t orow = (out_head + qrow) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1437,7 +1482,8 @@ struct Fwd32 {
                         f32x4_t{acc[db][4 * jj] * inv, acc[db][4 * jj + 1] * inv,
                                 acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv};
                 }
-            if (lh == 0) p.lse[(size_t)hh * N + qrow] = (m * c + __log2f(lt)) * kLn2;
+            if (lh == 0)
+                p.lse[out_head + qrow] = SPLIT && !(lt > 0.f) ? -__builtin_inff() : (m * c + __log2f(lt)) * kLn2;
         }
         if (COUNT && tid == 0) add_tile_counts<BQ, BK, CAUSAL>(p.counters, qt0, jend, N);
     }

@@ -73,6 +73,9 @@ FA_DECLARE_TILE(256, 128)
 #undef FA_DECLARE_TILE
 int launch32_c0(const FwdParams& p, int d, bool count, void* stream);
 int launch32_c1(const FwdParams& p, int d, bool count, void* stream);
+// fp32 split-KV (partials and merge; 64-row query tiles)
+int launch32s_c0(const FwdParams& p, int d, void* o, float* lse, void* stream);
+int launch32s_c1(const FwdParams& p, int d, void* o, float* lse, void* stream);
 
 // The current device: FA_OK if it is a gfx950 (and its compute-unit count
 // in *cus), FA_ERR_UNSUPPORTED otherwise, FA_ERR_HIP if the query fails.
