@@ -371,7 +371,25 @@ def cpu_baseline(seconds):
     return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=f"{heads} head(s) of N={N}, d={d}, non-causal, float64 with S and P "
                        f"materialised, {t_total:.1f} s",
-                seconds=t_total)
+                seconds=t_total, host=host_cpu())
+
+
+def host_cpu():
+    """The host's CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "usable_cores": usable}
 
 
 def read_summary(path):
