@@ -24,9 +24,10 @@ struct f16 { using T = F16; };
 template <class T, int D, bool C>
 int launch(const BwdParams& p0, int heads, void* stream) {
     BwdParams p = p0;
+    p.nblk = (p.N + DqShape<D>::ROWS - 1) / DqShape<D>::ROWS;
     p.nblk_k = (p.N + DkdvShape<D>::KEYS - 1) / DkdvShape<D>::KEYS;
     const hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL((dq_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((dq_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk)), dim3(DqShape<D>::NT), 0, st, p);
     hipLaunchKernelGGL((dkdv_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk_k)), dim3(DkdvShape<D>::NT), 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -10,8 +10,9 @@
 //
 // Two kernels, launched in this order on one stream:
 //
-//   dq_kernel    one workgroup = 128 query rows of one head (4 waves x 32
-//                rows); the wave's Q and dO rows stay in registers, K and V
+//   dq_kernel    one workgroup = 256 query rows of one head at d = 128 (8
+//                waves x 32 rows; 128 rows and 4 waves at d = 64); the
+//                wave's Q and dO rows stay in registers, K and V
 //                tiles of 64 keys pass through LDS.  Per 32-key block it
 //                computes S^T = K Q^T and dP^T = V dO^T (a lane holds one
 //                query), dS^T, and dQ^T += K^T dS^T; it also computes D for
@@ -59,7 +60,7 @@ struct BwdParams {
     float* delta;
     int N;
     int heads;     // B * H
-    int nblk;      // 128-row query blocks per head (dq_kernel)
+    int nblk;      // query blocks per head (dq_kernel, DqShape<D>::ROWS rows each)
     int nblk_k;    // key blocks per head (dkdv_kernel, DkdvShape<D>::KEYS keys each)
     float c;       // scale * log2(e)
     float scale;
@@ -168,10 +169,21 @@ __device__ __forceinline__ void store_rows(uint16_t* out, int row, int N, const 
         }
 }
 
+// Shape of dq_kernel: query rows per workgroup, 32 per wave.  Eight waves
+// at d = 128 (one workgroup per CU at two waves per SIMD) copy each K / V
+// tile into LDS once per 256 rows instead of once per 128.
+template <int D>
+struct DqShape {
+    static constexpr int WAVES = D == 128 ? 8 : 4;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int ROWS = 32 * WAVES;
+};
+
 template <class T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3)))
-dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(DqShape<D>::NT)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kernel(BwdParams p) {
     using G = Geo<D>;
+    constexpr int ROWS = DqShape<D>::ROWS, NT = DqShape<D>::NT;
     // K and V tiles, double-buffered
     __shared__ __attribute__((aligned(16))) uint8_t ks[2][G::TILE * G::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t vs[2][G::TILE * G::PITCH];
@@ -187,7 +199,7 @@ dq_kernel(BwdParams p) {
         hh = L / p.nblk;
         qb = L - hh * p.nblk;
     }
-    const int q0 = qb * 128, qw = q0 + 32 * wave, q = qw + li;
+    const int q0 = qb * ROWS, qw = q0 + 32 * wave, q = qw + li;
     const size_t head = (size_t)hh * N * D;
     const uint32_t hb = (uint32_t)N * D * 2;
     const auto rq = make_rsrc(p.q + head, hb), rk = make_rsrc(p.k + head, hb), rv = make_rsrc(p.v + head, hb);
@@ -213,9 +225,9 @@ dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16_t{};
 
-    const int kend = CAUSAL ? min(N, q0 + 128) : N;
+    const int kend = CAUSAL ? min(N, q0 + ROWS) : N;
     const int nkt = (kend + G::TILE - 1) / G::TILE;
-    TileRegs<D> kr, vr;
+    TileRegs<D, NT> kr, vr;
     kr.load(rk, 0, tid);
     vr.load(rv, 0, tid);
     kr.store(ks[0], tid);
