@@ -341,7 +341,7 @@ const char* fa_build_info(void) {
            "; kernels: bf16/f16 d64 and d128 (256x64 tiles non-causal, 128x64 causal, 32 query rows per wave; "
            "persistent across query tiles without a mask), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off; "
-           "split-KV bf16/f16 d64/d128 causal on/off (fp32 partials + merge); "
+           "split-KV bf16/f16/f32 d64/d128 causal on/off (fp32 partials + merge); "
            "backward bf16/f16 d64/d128 causal on/off (dQ kernel, dK/dV kernel); "
            "standard materialising forward bf16/f16 d64/d128 (scores, softmax, output)";
 }
