@@ -245,3 +245,30 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import oracle|from oracle)", text, flags=re.M), f
+
+
+def test_preallocated_outputs_are_checked():
+    """attention() hands o and lse to the kernel as raw pointers: buffers of
+    the wrong type, size, layout or device are refused before any launch."""
+    import torch
+    q = torch.empty((2, 3, 100, 64), dtype=torch.bfloat16)
+    good_o, good_lse = torch.empty_like(q), torch.empty((2, 3, 100), dtype=torch.float32)
+    fa.check_outputs(q, good_o, good_lse)
+    fa.check_outputs(q, torch.empty(q.shape, dtype=torch.float32), good_lse, out_f32=True)
+    bad_o = [torch.empty(q.shape, dtype=torch.float32),                 # fp32 without out_f32
+             torch.empty((2, 3, 99, 64), dtype=torch.bfloat16),         # too small
+             torch.empty((2, 3, 64, 100), dtype=torch.bfloat16).transpose(2, 3)]   # strided
+    for o in bad_o:
+        with pytest.raises(ValueError):
+            fa.check_outputs(q, o, good_lse)
+    with pytest.raises(ValueError):
+        fa.check_outputs(q, good_o, good_lse, out_f32=True)             # bf16 o for an fp32 launch
+    bad_lse = [torch.empty((2, 3, 100), dtype=torch.float16),
+               torch.empty((2, 3, 50), dtype=torch.float32),
+               torch.empty((2, 100, 3), dtype=torch.float32).transpose(1, 2)]
+    for lse in bad_lse:
+        with pytest.raises(ValueError):
+            fa.check_outputs(q, good_o, lse)
+    if torch.cuda.is_available():
+        with pytest.raises(ValueError):
+            fa.check_outputs(q.cuda(), good_o, good_lse)               # host buffers for a device launch

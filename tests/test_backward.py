@@ -51,7 +51,7 @@ def grad_errors(dev, ref, dtype):
     out = {}
     for name, g, r in zip(("dq", "dk", "dv"), dev, ref):
         scale = float(np.max(np.abs(r))) or 1.0
-        ex = float(np.max(np.abs(g - r) - half_ulp(np.maximum(np.abs(r), np.abs(g)), dtype))) if r.size else 0.0
+        ex = float(np.max(np.abs(g - r) - half_ulp(r, dtype))) if r.size else 0.0
         out[name] = ex / scale
     return out
 

@@ -266,6 +266,22 @@ def dtype_code(torch_dtype):
     return codes[torch_dtype]
 
 
+def check_outputs(q, o=None, lse=None, out_f32=False):
+    """Raises ValueError unless caller-supplied output buffers fit the launch
+    for ``q``: the kernel writes B*H*N*d elements of O (fp32 when ``out_f32``,
+    else q's type) and B*H*N fp32 LSE values through raw pointers, so a
+    smaller, strided, mistyped or foreign-device buffer would be overrun."""
+    import torch
+    B, H, N, _ = q.shape
+    o_dtype = torch.float32 if out_f32 else q.dtype
+    if o is not None and (o.dtype != o_dtype or o.shape != q.shape or not o.is_contiguous()
+                          or o.device != q.device):
+        raise ValueError(f"o must be a contiguous {o_dtype} tensor of shape {tuple(q.shape)} on {q.device}")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H, N)} on {q.device}")
+
+
 def attention(q, k, v, causal=False, scale=None, out_f32=False, counters=False,
               o=None, lse=None, stream=None, tile=None):
     """Exact attention forward on the device.
@@ -290,6 +306,7 @@ def attention(q, k, v, causal=False, scale=None, out_f32=False, counters=False,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = dtype_code(q.dtype)
+    check_outputs(q, o, lse, out_f32)
     if o is None:
         o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
     if lse is None:
