@@ -70,6 +70,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
            int dtype);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd
+ * without the delta argument.  The D work array lives in a fixed scratch
+ * array inside the library, FA_BWD_NOALLOC_MAX_ROWS fp32 values (16 MiB),
+ * one copy per device, held until the process ends; its address is resolved
+ * on the first call made with that device current.  The call allocates
+ * nothing and runs the same kernels as fa_bwd, so it returns the same bits.
+ *   B * H * N above FA_BWD_NOALLOC_MAX_ROWS -> FA_ERR_SCRATCH, before any HIP
+ *   call; every other argument and error as for fa_bwd.
+ * All calls on one device share that device's scratch array: calls that
+ * overlap in time on one device (different streams, or host threads without
+ * ordering) race on it and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero; each call writes D before reading it.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* stream,
+                   int dtype);
+
 #ifdef __cplusplus
 }
 #endif

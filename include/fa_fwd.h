@@ -64,8 +64,11 @@ typedef enum {
     FA_ERR_UNSUPPORTED = 2,  /* d not 64 or 128, unknown dtype, tile shape not
                                 built, sizes beyond the limits above, device
                                 not gfx950                                    */
-    FA_ERR_HIP = 3           /* a HIP runtime call (device query or kernel
+    FA_ERR_HIP = 3,          /* a HIP runtime call (device query or kernel
                                 launch) failed                               */
+    FA_ERR_SCRATCH = 4       /* the problem needs more work memory than the
+                                fixed scratch array of a no-allocation entry
+                                point holds (fa_bwd.h, fa_bwd_noalloc)       */
 } fa_status;
 
 /* Element types of q, k, v (and of o unless out_dtype says fp32). */

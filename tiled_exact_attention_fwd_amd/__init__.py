@@ -59,7 +59,10 @@ SIGNATURES = {
     "fa_bwd_f16": (_I, _BWD17),
     "fa_bwd_f32": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
+    "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _I]),
 }
+FA_ERR_SCRATCH = 4
+BWD_NOALLOC_MAX_ROWS = 1 << 22
 
 
 class FaLibraryMissing(ImportError):
@@ -203,6 +206,10 @@ def fa_bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, caus
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype):
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream, dtype):
+    return lib().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream, dtype)
 
 
 def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):

@@ -3,8 +3,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_bwd.h"
 #include "fa_bwd32_kernels.h"
@@ -13,7 +15,40 @@
 #include "fa_fwd.h"
 #include "fa_fwd_launch.h"
 
+// Work memory of fa_bwd_noalloc: the D array (one fp32 per query row of the
+// launch), for callers that cannot allocate.  Every device the library runs
+// on holds its own copy until the process ends.  In host code the name is a
+// stand-in, not a device address: the address of the current device's copy
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// handed to kernels.
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<float*> g_scratch[kMaxDevices];   // device address of each device's copy
+
+// The current device's copy of `scratch`, resolved on the first call made
+// with that device current.
+int scratch_for_current_device(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    float* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            void* addr = nullptr;
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return FA_ERR_HIP;
+            ptr = (float*)addr;
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return FA_OK;
+}
 
 bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -22,8 +57,9 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 
 int run(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
         void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
-        int dtype) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_INVALID;
+        int dtype, bool noalloc = false) {
+    // noalloc: delta is ignored and the D array lives in `scratch`
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (!noalloc && !delta)) return FA_ERR_INVALID;
     if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID;
     if (!std::isfinite(scale)) return FA_ERR_INVALID;
@@ -40,15 +76,21 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     const uint64_t inb[6] = {tb, tb, tb, tb, tb, sb};
     void* outs[4] = {dq, dk, dv, delta};
     const uint64_t outb[4] = {tb, tb, tb, sb};
-    for (int i = 0; i < 4; ++i) {
+    const int nouts = noalloc ? 3 : 4;
+    for (int i = 0; i < nouts; ++i) {
         for (int j = 0; j < 6; ++j)
             if (overlaps(outs[i], outb[i], ins[j], inb[j])) return FA_ERR_INVALID;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < nouts; ++j)
             if (overlaps(outs[i], outb[i], outs[j], outb[j])) return FA_ERR_INVALID;
     }
+    if (noalloc && heads * N > (uint64_t)FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
     int cus = 0;
     const int dev_st = fa::device_check(&cus);
     if (dev_st != FA_OK) return dev_st;
+    if (noalloc) {
+        const int sst = scratch_for_current_device(&delta);
+        if (sst != FA_OK) return sst;
+    }
     if (dtype == FA_DTYPE_F32) {
         fa::bwd::BwdParams32 p32;
         p32.q = (const float*)q; p32.k = (const float*)k; p32.v = (const float*)v;
@@ -88,6 +130,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
            int dtype) {
     return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* stream,
+                   int dtype) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, H, N, d, scale, causal, stream, dtype, true);
 }
 
 int fa_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

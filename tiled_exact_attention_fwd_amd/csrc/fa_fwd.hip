@@ -332,6 +332,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_INVALID: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_SCRATCH: return "problem exceeds the fixed scratch array of a no-allocation entry point";
     default: return "unknown status";
     }
 }
