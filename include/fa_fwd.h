@@ -123,9 +123,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *              FA_ERR_UNSUPPORTED otherwise.
  *   counters   NULL for the plain kernel; otherwise a device array of
  *              FA_NUM_COUNTERS unsigned 64-bit integers to which the launch
- *              ADDS its tile counts (indices above).  The caller zeroes it.
- *              A separately compiled instrumented kernel is used; the plain
- *              kernel carries no counting code.
+ *              ADDS its tile counts (indices above), in the tile of
+ *              fa_fwd_launch_tile: each (query tile, key tile) pair the
+ *              kernel's loop processes is counted and classed, and the
+ *              pairs of each processed query tile that the loop does not
+ *              visit are counted as skipped.  The caller zeroes it.  A
+ *              separately compiled instrumented instance of the kernel the
+ *              plain launch runs is used; the plain kernel carries no
+ *              counting code.
  */
 typedef struct {
     const void* q;
@@ -174,12 +179,31 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, int splits, void* stream, int dtype);
 
 /*
- * The (tile_q, tile_k) shape a launch with these parameters uses by default,
- * so the caller can compute the expected tile counts.  Pure host function,
- * no HIP call.  Returns FA_OK, or FA_ERR_UNSUPPORTED / FA_ERR_INVALID with
- * the outputs untouched.
+ * The (tile_q, tile_k) shape of the per-tile kernel for these parameters:
+ * the tile of fp32-output launches and of launches too small for the
+ * persistent kernels (fa_fwd_launch_tile gives the tile of any launch).
+ * Pure host function, no HIP call.  Returns FA_OK, or FA_ERR_UNSUPPORTED /
+ * FA_ERR_INVALID with the outputs untouched.
  */
 int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k);
+
+/*
+ * The (tile_q, tile_k) tile that fa_fwd_ex(args) would work in on the
+ * current device -- the unit of its tile counters, so that the caller can
+ * compute the expected counts for exactly that tiling (block counting of
+ * §2.2 of "FlashAttention分块计算优化Transformer显存效率" at B_q = tile_q,
+ * B_k = tile_k).  The choice depends on B * H, N, the mask, the output type
+ * and the device's compute-unit count: 16-bit launches that fill the device
+ * run persistent kernels (256 x 64 without a mask; 256 x 64 causal at
+ * d = 128; 128 x 64 causal at d = 64), the others the per-tile kernels
+ * (fa_fwd_tile_shape).  A launch with counters runs the instrumented
+ * instance of the kernel the same launch without counters runs.
+ * Nothing is launched; args->counters is not read.  The arguments are
+ * checked as by fa_fwd_ex (same error codes); then the device is queried
+ * (cached): FA_ERR_UNSUPPORTED if it is not gfx950, FA_ERR_HIP if the query
+ * fails.  FA_ERR_INVALID for a NULL tile_q or tile_k.
+ */
+int fa_fwd_launch_tile(const fa_fwd_args* args, int* tile_q, int* tile_k);
 
 /* Static description of a status code; never NULL. */
 const char* fa_strerror(int status);

@@ -69,13 +69,13 @@ def assert_gates(errs, dtype, what=""):
     assert errs["lse"] <= TOL_LSE, msg
 
 
-def sample_rows(N, tile, rng, n_random=24):
-    """Rows 0, 1, N-1, both sides of every tile boundary (capped), and random
-    rows."""
+def sample_rows(N, tile, rng, n_random=24, cap=None):
+    """Rows 0, 1, N-1, N-2, both sides of every multiple of `tile` (of `cap`
+    randomly chosen ones when a cap is given), and random rows."""
     rows = {0, 1, N - 1, N - 2}
     bounds = list(range(tile, N, tile))
-    if len(bounds) > 24:
-        bounds = list(rng.choice(bounds, 24, replace=False))
+    if cap is not None and len(bounds) > cap:
+        bounds = list(rng.choice(bounds, cap, replace=False))
     for b in bounds:
         rows.update({b - 1, b})
     rows.update(rng.choice(N, min(N, n_random), replace=False).tolist())

@@ -320,3 +320,26 @@ def test_preallocated_outputs_are_checked():
     if torch.cuda.is_available():
         with pytest.raises(ValueError):
             fa.check_outputs(q.cuda(), good_o, good_lse)               # host buffers for a device launch
+
+
+def test_launch_tile_argument_checks():
+    """fa_fwd_launch_tile checks its arguments as fa_fwd_ex does, before any
+    HIP call; with valid arguments it needs the device (its compute units
+    decide between the persistent and the per-tile kernels)."""
+    def lt(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+                 stream=None, dtype=fa.FA_DTYPE_BF16)
+        a.update(over)
+        return fa.fa_fwd_launch_tile(**a)
+    assert lt(B=0)[0] == fa.FA_ERR_INVALID
+    assert lt(q=None)[0] == fa.FA_ERR_INVALID
+    assert lt(o=Q)[0] == fa.FA_ERR_INVALID
+    assert lt(causal=3)[0] == fa.FA_ERR_INVALID
+    assert lt(d=96)[0] == fa.FA_ERR_UNSUPPORTED
+    assert lt(tile_q=32, tile_k=64)[0] == fa.FA_ERR_UNSUPPORTED
+    a = fa.FaArgs(Q, K, V, O, L, 2, 3, 100, 64, 0.125, 0, None, fa.FA_DTYPE_BF16, 0, 0, 0, None)
+    t = ctypes.c_int(0)
+    assert fa.lib().fa_fwd_launch_tile(ctypes.byref(a), None, ctypes.byref(t)) == fa.FA_ERR_INVALID
+    assert fa.lib().fa_fwd_launch_tile(None, ctypes.byref(t), ctypes.byref(t)) == fa.FA_ERR_INVALID
+    if NO_GPU:
+        assert lt()[0] == fa.FA_ERR_HIP

@@ -231,7 +231,7 @@ def test_long_context_sampled_rows():
     _, (dq, dk, dv, _) = run_device(words, dwords, wl.dtype, True, scale)
     rng = np.random.default_rng(77)
     qr = np.arange(N)
-    kr = sample_rows(N, 256, rng, n_random=16)
+    kr = sample_rows(N, 256, rng, n_random=16, cap=24)
     b, h = 0, H - 1
     vals = [W.decode64(w[b, h], wl.dtype) for w in (*words, dwords)]
     ref = oracle.attention_bwd_sampled(*vals, scale, True, qr, kr, chunk=1024)
@@ -284,7 +284,7 @@ def test_maximum_size():
     rng = np.random.default_rng(10)
     # the first rows carry the largest dQ entries (the gate's scale), then
     # tile edges and random rows
-    qr = np.unique(np.concatenate([np.arange(64), sample_rows(N, 256, rng, n_random=8)]))
+    qr = np.unique(np.concatenate([np.arange(64), sample_rows(N, 256, rng, n_random=8, cap=24)]))
     vals = [W.decode64(w[0, 0], "bf16") for w in (*words, dwords)]
     ref, _, _ = oracle.attention_bwd_sampled(*vals, W.scale_for(d), True, qr, [], chunk=64)
     print(f"  oracle rows done ({time.time() - t0:.0f} s)", flush=True)

@@ -51,6 +51,7 @@ SIGNATURES = {
     "fa_fwd": (_I, _FWD12 + [_I]),
     "fa_fwd_ex": (_I, [ctypes.POINTER(FaArgs)]),
     "fa_fwd_tile_shape": (_I, [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "fa_fwd_launch_tile": (_I, [ctypes.POINTER(FaArgs), ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_build_info": (ctypes.c_char_p, []),
     "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
@@ -60,6 +61,7 @@ SIGNATURES = {
     "fa_bwd_f32": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
     "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _I]),
+    "fa_clock_probe": (_I, [_P, ctypes.c_uint, _P]),
 }
 FA_ERR_SCRATCH = 4
 BWD_NOALLOC_MAX_ROWS = 1 << 22
@@ -247,10 +249,25 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
     return dq, dk, dv, delta
 
 
+def fa_clock_probe(out, ticks, stream):
+    return lib().fa_clock_probe(out, ticks, stream)
+
+
 def fa_fwd_tile_shape(dtype, d, causal):
     """Returns ``(status, tile_q, tile_k)``."""
     tq, tk = _I(0), _I(0)
     st = lib().fa_fwd_tile_shape(dtype, d, causal, ctypes.byref(tq), ctypes.byref(tk))
+    return st, tq.value, tk.value
+
+
+def fa_fwd_launch_tile(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
+                       out_dtype=0, tile_q=0, tile_k=0, counters=None):
+    """Returns ``(status, tile_q, tile_k)``: the tile of the kernel that
+    ``fa_fwd_ex`` with these arguments runs."""
+    a = FaArgs(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype,
+               out_dtype, tile_q, tile_k, counters)
+    tq, tk = _I(0), _I(0)
+    st = lib().fa_fwd_launch_tile(ctypes.byref(a), ctypes.byref(tq), ctypes.byref(tk))
     return st, tq.value, tk.value
 
 

@@ -105,6 +105,59 @@ int check_device(int* cus) {
     return st == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
 }
 
+// The kernel a launch runs, chosen from the arguments and the device's
+// compute units; a launch with tile counters takes the same choice (the
+// instrumented instance of the same kernel), so its counts are those of the
+// kernel the plain launch runs.
+enum LaunchKind { kSweep, kPersistent, kPersistentCausalWide, kPersistentCausal, kPerTile16, kPerTile32 };
+struct LaunchPlan {
+    LaunchKind kind;
+    int tq, tk;     // query rows and keys of the tile the kernel works in
+    int grid;       // workgroups of a persistent kernel (0: one per query tile)
+};
+
+LaunchPlan plan_launch(const fa_fwd_args* a, int cus) {
+    int tq, tk;
+    launch_shape(a, &tq, &tk);
+    const bool c = a->causal != 0, o32 = a->out_dtype != 0, f32 = a->dtype == FA_DTYPE_F32;
+    if (f32) return {kPerTile32, tq, tk, 0};
+    // an explicitly requested tile-size sweep shape: the per-tile kernel of
+    // that shape (for the default shape too, so that a sweep compares one
+    // kernel family)
+    if (a->tile_q && sweep_shape(a, tq, tk)) return {kSweep, tq, tk, 0};
+    const long long heads = (long long)a->B * a->H;
+    // A 16-bit launch without a mask that has more query tiles than the
+    // device has workgroup slots runs the persistent kernel: one workgroup
+    // per slot (a multiple of 8, so that each keeps to one XCD's tiles) takes
+    // every slots-th query tile and pipelines across them.
+    const int slots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(false);
+    const int nk = (a->N + tk - 1) / tk;
+    const long long tiles = heads * ((a->N + tq - 1) / tq);
+    if (!c && !o32 && slots > 0 && tiles > slots && nk >= fa::persistent_min_key_tiles())
+        return {kPersistent, tq, tk, slots};
+    // Under the causal mask at d = 128: the persistent kernel with 256-row
+    // query tiles (one workgroup per CU), each work unit a pair of query
+    // tiles (i, T - 1 - i) of one head, whose key tiles add up to the same
+    // count for every pair; the shortest tile must have 4 key tiles.
+    if (c && a->d == 128 && !o32 && slots > 0) {
+        const int tw = fa::wide_tile_q(), wtiles = (a->N + tw - 1) / tw;
+        const int nk_first = (std::min(tw, a->N) - 1) / tk + 1;
+        if (wtiles % 2 == 0 && nk_first >= 4 && heads * wtiles / 2 > slots)
+            return {kPersistentCausalWide, tw, tk, slots};
+    }
+    // Likewise under the causal mask at d = 64, where two workgroups per CU
+    // fit their K, V, Q and output staging in LDS: each takes pairs of query
+    // tiles (i, T - 1 - i) of equal total cost, so T must be even.  Only for
+    // rows of at most 16 key tiles: measured 4% faster at N = 1000, but 1-3%
+    // slower from N = 2048 on, where the per-tile kernel's two co-resident
+    // workgroups already hide most of the per-tile cost.
+    const int cslots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(true);
+    const int tiles_q = (a->N + tq - 1) / tq;
+    if (c && a->d == 64 && !o32 && cslots > 0 && tiles_q % 2 == 0 && tiles / 2 > cslots && nk <= 16)
+        return {kPersistentCausal, tq, tk, cslots};
+    return {kPerTile16, tq, tk, 0};
+}
+
 int run(const fa_fwd_args* a) {
     int st = check_args(a);
     if (st != FA_OK) return st;
@@ -112,9 +165,7 @@ int run(const fa_fwd_args* a) {
     st = check_device(&cus);
     if (st != FA_OK) return st;
 
-    int tq, tk, dq, dk;
-    launch_shape(a, &tq, &tk);
-    tile_shape(a->dtype, a->d, a->causal, &dq, &dk);
+    const LaunchPlan plan = plan_launch(a, cus);
     FwdParams p;
     p.q = a->q;
     p.k = a->k;
@@ -122,7 +173,7 @@ int run(const fa_fwd_args* a) {
     p.o = a->o;
     p.lse = a->lse;
     p.N = a->N;
-    p.tiles_q = (a->N + tq - 1) / tq;
+    p.tiles_q = (a->N + plan.tq - 1) / plan.tq;
     p.heads = a->B * a->H;
     p.total = p.heads * p.tiles_q;
     const int resident = a->dtype == FA_DTYPE_F32 ? fa::resident32() : fa::resident16(a->causal != 0);
@@ -136,13 +187,12 @@ int run(const fa_fwd_args* a) {
     p.splits = 1;
     p.split_len = a->N;
     const bool count = a->counters != nullptr;
-
+    const bool bf = a->dtype == FA_DTYPE_BF16, d64 = a->d == 64;
     const int c = a->causal, o32 = a->out_dtype;
-    if (a->tile_q && sweep_shape(a, tq, tk)) {
-        // an explicitly requested tile-size sweep shape: the per-tile kernel
-        // of that shape (for the default shape too, so that a sweep compares
-        // one kernel family)
-        switch (tq * 1000 + tk) {
+
+    switch (plan.kind) {
+    case kSweep:
+        switch (plan.tq * 1000 + plan.tk) {
         case 256064: return fa::launch16_bf16_d128_c0(p, 0, count, a->stream);
         case 64032: return fa::launch16t_q64_k32(p, count, a->stream);
         case 64064: return fa::launch16t_q64_k64(p, count, a->stream);
@@ -154,60 +204,46 @@ int run(const fa_fwd_args* a) {
         case 256128: return fa::launch16t_q256_k128(p, count, a->stream);
         default: return FA_ERR_UNSUPPORTED;
         }
-    }
-    // A plain 16-bit launch without a mask that has more query tiles than
-    // the device has workgroup slots runs the persistent kernel: one
-    // workgroup per slot (a multiple of 8, so that each keeps to one XCD's
-    // tiles) takes every slots-th query tile and pipelines across them.
-    const int slots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(false);
-    const int nk = (a->N + tk - 1) / tk;
-    if (!c && a->dtype != FA_DTYPE_F32 && !o32 && !count && slots > 0 && p.total > slots &&
-        nk >= fa::persistent_min_key_tiles()) {
-        if (a->dtype == FA_DTYPE_BF16)
-            return a->d == 64 ? fa::launch16p_bf16_d64(p, slots, a->stream) : fa::launch16p_bf16_d128(p, slots, a->stream);
-        return a->d == 64 ? fa::launch16p_f16_d64(p, slots, a->stream) : fa::launch16p_f16_d128(p, slots, a->stream);
-    }
-    // Under the causal mask at d = 128: the persistent kernel with 256-row
-    // query tiles (one workgroup per CU), each work unit a pair of query
-    // tiles (i, T - 1 - i) of one head, whose key tiles add up to the same
-    // count for every pair; the shortest tile must have 4 key tiles.
-    if (c && a->d == 128 && a->dtype != FA_DTYPE_F32 && !o32 && !count && slots > 0) {
-        const int tw = 256, tiles = (a->N + tw - 1) / tw;
-        const int nk_first = (std::min(tw, a->N) - 1) / tk + 1;
-        if (tiles % 2 == 0 && nk_first >= 4 && p.heads * tiles / 2 > slots) {
-            FwdParams pw = p;
-            pw.tiles_q = tiles;
-            pw.total = p.heads * tiles;
-            return a->dtype == FA_DTYPE_BF16 ? fa::launch16pcw_bf16_d128(pw, slots, a->stream)
-                                             : fa::launch16pcw_f16_d128(pw, slots, a->stream);
+    case kPersistent:
+        if (bf) return d64 ? fa::launch16p_bf16_d64(p, plan.grid, count, a->stream)
+                           : fa::launch16p_bf16_d128(p, plan.grid, count, a->stream);
+        return d64 ? fa::launch16p_f16_d64(p, plan.grid, count, a->stream)
+                   : fa::launch16p_f16_d128(p, plan.grid, count, a->stream);
+    case kPersistentCausalWide:
+        return bf ? fa::launch16pcw_bf16_d128(p, plan.grid, count, a->stream)
+                  : fa::launch16pcw_f16_d128(p, plan.grid, count, a->stream);
+    case kPersistentCausal:
+        return bf ? fa::launch16pc_bf16_d64(p, plan.grid, count, a->stream)
+                  : fa::launch16pc_f16_d64(p, plan.grid, count, a->stream);
+    case kPerTile16:
+        if (bf) {
+            if (d64) return c ? fa::launch16_bf16_d64_c1(p, o32, count, a->stream)
+                              : fa::launch16_bf16_d64_c0(p, o32, count, a->stream);
+            return c ? fa::launch16_bf16_d128_c1(p, o32, count, a->stream)
+                     : fa::launch16_bf16_d128_c0(p, o32, count, a->stream);
         }
-    }
-    // Likewise under the causal mask at d = 64, where two workgroups per CU
-    // fit their K, V, Q and output staging in LDS: each takes pairs of query
-    // tiles (i, T - 1 - i) of equal total cost, so T must be even.  Only for
-    // rows of at most 16 key tiles: measured 4% faster at N = 1000, but 1-3%
-    // slower from N = 2048 on, where the per-tile kernel's two co-resident
-    // workgroups already hide most of the per-tile cost.
-    const int cslots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(true);
-    if (c && a->d == 64 && a->dtype != FA_DTYPE_F32 && !o32 && !count && cslots > 0 && p.tiles_q % 2 == 0 &&
-        p.total / 2 > cslots && nk <= 16) {
-        return a->dtype == FA_DTYPE_BF16 ? fa::launch16pc_bf16_d64(p, cslots, a->stream)
-                                         : fa::launch16pc_f16_d64(p, cslots, a->stream);
-    }
-    switch (a->dtype) {
-    case FA_DTYPE_BF16:
-        if (a->d == 64) return c ? fa::launch16_bf16_d64_c1(p, o32, count, a->stream)
-                                 : fa::launch16_bf16_d64_c0(p, o32, count, a->stream);
-        return c ? fa::launch16_bf16_d128_c1(p, o32, count, a->stream)
-                 : fa::launch16_bf16_d128_c0(p, o32, count, a->stream);
-    case FA_DTYPE_F16:
-        if (a->d == 64) return c ? fa::launch16_f16_d64_c1(p, o32, count, a->stream)
-                                 : fa::launch16_f16_d64_c0(p, o32, count, a->stream);
+        if (d64) return c ? fa::launch16_f16_d64_c1(p, o32, count, a->stream)
+                          : fa::launch16_f16_d64_c0(p, o32, count, a->stream);
         return c ? fa::launch16_f16_d128_c1(p, o32, count, a->stream)
                  : fa::launch16_f16_d128_c0(p, o32, count, a->stream);
-    default:
+    case kPerTile32:
         return c ? fa::launch32_c1(p, a->d, count, a->stream) : fa::launch32_c0(p, a->d, count, a->stream);
     }
+    return FA_ERR_UNSUPPORTED;
+}
+
+// The tile of the kernel a launch with these arguments runs.
+int launch_tile(const fa_fwd_args* a, int* tile_q, int* tile_k) {
+    if (!tile_q || !tile_k) return FA_ERR_INVALID;
+    int st = check_args(a);
+    if (st != FA_OK) return st;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FA_OK) return st;
+    const LaunchPlan plan = plan_launch(a, cus);
+    *tile_q = plan.tq;
+    *tile_k = plan.tk;
+    return FA_OK;
 }
 
 // Split-KV forward: argument checks, then the partial and merge kernels.
@@ -317,6 +353,8 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
     const fa_fwd_args a = plain_args(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
     return run_split(&a, o_part, lse_part, splits);
 }
+
+int fa_fwd_launch_tile(const fa_fwd_args* args, int* tile_q, int* tile_k) { return launch_tile(args, tile_q, tile_k); }
 
 int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k) {
     if (!tile_q || !tile_k || (causal != 0 && causal != 1)) return FA_ERR_INVALID;

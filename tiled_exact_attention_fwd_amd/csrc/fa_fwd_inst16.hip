@@ -51,23 +51,29 @@ int FA_XCAT6(launch16s_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)(const FwdParam
 #define FA_CAT4(a, b, c, d) a##b##c##d
 #define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
 #if FA_INST_C == 0
-// the persistent kernel (no mask, 16-bit output, no counters) on `grid` workgroups
-int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
-    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>::BQ == tile_q16(false), "grid tile");
-    return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>>(p, stream, grid);
+// the persistent kernel (no mask, 16-bit output) on `grid` workgroups; count:
+// its instrumented instance
+int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, bool count, void* stream) {
+    using K = Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>;
+    static_assert(K::BQ == tile_q16(false), "grid tile");
+    return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D>>(p, stream, grid)
+                 : launch_kernel<K>(p, stream, grid);
 }
 #elif FA_INST_D == 128
 // the causal persistent kernel with 256-row query tiles (d = 128, 16-bit
-// output, no counters)
-int FA_XCAT4(launch16pcw_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
-    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>::BQ == 256, "grid tile");
-    return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid);
+// output); count: its instrumented instance
+int FA_XCAT4(launch16pcw_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, bool count, void* stream) {
+    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>::BQ == wide_tile_q(), "grid tile");
+    return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid)
+                 : launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid);
 }
 #else
-// the causal persistent kernel (d = 64, 16-bit output, no counters)
-int FA_XCAT4(launch16pc_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, void* stream) {
+// the causal persistent kernel (d = 64, 16-bit output); count: its
+// instrumented instance
+int FA_XCAT4(launch16pc_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, bool count, void* stream) {
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>::BQ == tile_q16(true), "grid tile");
-    return launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid);
+    return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid)
+                 : launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid);
 }
 #endif
 

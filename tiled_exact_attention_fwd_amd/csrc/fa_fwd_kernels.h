@@ -1009,7 +1009,12 @@ struct Fwd16P {
         }
     }
 
-    static __device__ void run(const FwdParams& p) {
+    static __device__ void run(const FwdParams& p) { run_impl<false>(p); }
+
+    // COUNT: the instrumented instance (Fwd16PCount) adds the tile counts of
+    // the (query tile, key tile) pairs its iterations process to p.counters
+    template <bool COUNT>
+    static __device__ void run_impl(const FwdParams& p) {
         __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILEB];
         __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILEB];
         __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILEB];
@@ -1034,6 +1039,9 @@ struct Fwd16P {
         const uint8_t* const vptr = (const uint8_t*)pin_s(p.v);
         const int tiles_q = pin_s(p.tiles_q);
         const int total = pin_s(p.total);
+        unsigned long long* const counters = COUNT ? pin_s(p.counters) : nullptr;
+        // tile counts of the pairs processed: full, causal-masked, ragged, skipped
+        uint32_t n_full = 0, n_masked = 0, n_ragged = 0, n_skipped = 0;
 
         const int G = gridDim.x, b = blockIdx.x;
         // work units: query tiles, or (causal) pairs of query tiles; b < units
@@ -1235,6 +1243,17 @@ struct Fwd16P {
                 vc_ptr = vptr + cur.hoff + vcopy;
                 vc_ext = head_bytes - vcopy;
             }
+            if constexpr (COUNT) {
+                // the pair (query tile k0, key tile j0) whose softmax this
+                // iteration runs, classed as in add_tile_counts
+                if (j0 >= 0 && j0 < cur.nk && k0 < ntiles) {
+                    if (j0 == 0) n_skipped += (uint32_t)(nk_all - cur.nk);
+                    const int kk = j0 * BK;
+                    if (CAUSAL && kk + BK - 1 > cur.qt0) ++n_masked;
+                    else if (kk + BK > N) ++n_ragged;
+                    else ++n_full;
+                }
+            }
             st.meff = sm_on ? st.mc : __builtin_inff();
             st.lt = 0.f;
             const auto rkt = make_rsrc(kc_ptr, kc_ext);
@@ -1294,7 +1313,21 @@ struct Fwd16P {
         // the last tile's output (its LSE was stored at the iteration g = gend)
         __syncthreads();
         store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
+        if (COUNT && tid == 0) {
+            atomicAdd(counters + 0, (unsigned long long)(n_full + n_masked + n_ragged));
+            atomicAdd(counters + 1, (unsigned long long)n_full);
+            atomicAdd(counters + 2, (unsigned long long)n_masked);
+            atomicAdd(counters + 3, (unsigned long long)n_ragged);
+            atomicAdd(counters + 4, (unsigned long long)n_skipped);
+        }
     }
+};
+
+// The instrumented persistent kernel: the same code, plus the tile counts of
+// the pairs its iterations process (p.counters, as in Fwd16 with COUNT).
+template <class T, int D, bool CAUSAL = false, bool WIDE = false>
+struct Fwd16PCount : Fwd16P<T, D, CAUSAL, WIDE> {
+    static __device__ void run(const FwdParams& p) { Fwd16P<T, D, CAUSAL, WIDE>::template run_impl<true>(p); }
 };
 
 // ---------------------------------------------------------------------------

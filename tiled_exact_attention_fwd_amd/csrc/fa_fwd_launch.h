@@ -32,20 +32,22 @@ FA_DECLARE16(f16, 64, 1)
 FA_DECLARE16(f16, 128, 0)
 FA_DECLARE16(f16, 128, 1)
 #undef FA_DECLARE16
-// persistent kernels (no mask, 16-bit output, no counters; at least
-// persistent_min_key_tiles() key tiles), launched on `grid` workgroups
-int launch16p_bf16_d64(const FwdParams& p, int grid, void* stream);
-int launch16p_bf16_d128(const FwdParams& p, int grid, void* stream);
-int launch16p_f16_d64(const FwdParams& p, int grid, void* stream);
-int launch16p_f16_d128(const FwdParams& p, int grid, void* stream);
+// persistent kernels (no mask, 16-bit output; at least
+// persistent_min_key_tiles() key tiles), launched on `grid` workgroups;
+// count selects the instrumented instance
+int launch16p_bf16_d64(const FwdParams& p, int grid, bool count, void* stream);
+int launch16p_bf16_d128(const FwdParams& p, int grid, bool count, void* stream);
+int launch16p_f16_d64(const FwdParams& p, int grid, bool count, void* stream);
+int launch16p_f16_d128(const FwdParams& p, int grid, bool count, void* stream);
 constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TILES; }
 // causal persistent kernels (d = 64; an even number of query tiles, paired)
-int launch16pc_bf16_d64(const FwdParams& p, int grid, void* stream);
-int launch16pc_f16_d64(const FwdParams& p, int grid, void* stream);
+int launch16pc_bf16_d64(const FwdParams& p, int grid, bool count, void* stream);
+int launch16pc_f16_d64(const FwdParams& p, int grid, bool count, void* stream);
 // causal persistent kernels with 256-row query tiles (d = 128; an even number
 // of query tiles, paired; every query tile at least 4 key tiles)
-int launch16pcw_bf16_d128(const FwdParams& p, int grid, void* stream);
-int launch16pcw_f16_d128(const FwdParams& p, int grid, void* stream);
+constexpr int wide_tile_q() { return Fwd16P<BF16, 128, true, true>::BQ; }
+int launch16pcw_bf16_d128(const FwdParams& p, int grid, bool count, void* stream);
+int launch16pcw_f16_d128(const FwdParams& p, int grid, bool count, void* stream);
 // split-KV launches: p.o / p.lse point at the fp32 partials ([p.splits,
 // B H, N] x d and [p.splits, B H, N]); the merge writes o and lse
 #define FA_DECLARE16S(T, D, C) \
