@@ -31,7 +31,8 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 INFO = " ".join(COMMON_FLAGS + DEVICE_FLAGS)
 
 # (object name, source, defines)
-UNITS = [("fa_fwd", "fa_fwd.hip", [f'-DFA_BUILD_FLAGS="{INFO}"']), ("fa_standard", "fa_standard.hip", [])]
+UNITS = [("fa_fwd", "fa_fwd.hip", [f'-DFA_BUILD_FLAGS="{INFO}"']), ("fa_standard", "fa_standard.hip", []),
+         ("fa_probe", "fa_probe.hip", [])]
 for t in ("bf16", "f16"):
     for d in (64, 128):
         for c in (0, 1):
