@@ -499,6 +499,59 @@ def summarize(kind, paths):
             print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {avg} |")
         return
+    if kind == "pmc":
+        # 'pmc DIR...': rocprofv3 --pmc runs of --profile-run, each with its own
+        # counters; per forward kernel the median over its dispatches, and
+        # the ratios that locate its cycles
+        vals = {}
+        for d in paths:
+            for r in rows(d, "*counter_collection.csv"):
+                if "fa::" not in r["Kernel_Name"]:
+                    continue
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+        for name, cs in sorted(vals.items()):
+            med = {c: statistics.median(v) for c, v in cs.items()}
+            print(f"## {name}")
+            print()
+            print("| counter | dispatches | median per dispatch |")
+            print("|---|---|---|")
+            for c in sorted(med):
+                print(f"| {c} | {len(cs[c])} | {med[c]:.6g} |")
+            print()
+            ratio = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "SQ_CYCLES" in med:
+                ratio.append(("MFMA busy / SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / SQ_CYCLES)",
+                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_CYCLES"]))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+                ratio.append(("MFMA busy / (GRBM_GUI_ACTIVE x 1024 SIMDs)",
+                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * 1024)))
+            if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+                ratio.append(("matrix FLOPs (MOPS_BF16 x 512)", med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512))
+            if "SQ_INSTS_MFMA" in med:
+                for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_SMEM", "SQ_INSTS_VALU_TRANS_F32",
+                          "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VMEM"):
+                    if c in med:
+                        ratio.append((f"{c} per MFMA", med[c] / med["SQ_INSTS_MFMA"]))
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in med and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+                ratio.append(("cycles with a VALU issue under a busy MFMA / MFMA busy cycles",
+                              med["SQ_VALU_MFMA_COEXEC_CYCLES"] / med["SQ_VALU_MFMA_BUSY_CYCLES"]))
+            if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+                ratio.append(("LDS bank-conflict cycles / LDS active cycles",
+                              med["SQ_LDS_BANK_CONFLICT"] / max(med["SQ_LDS_IDX_ACTIVE"], 1)))
+            if "SQ_WAIT_INST_ANY" in med and "SQ_WAVE_CYCLES" in med:
+                ratio.append(("wave cycles waiting for an instruction's issue / wave cycles",
+                              med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"]))
+            if "SQ_ACTIVE_INST_VALU" in med and "SQ_WAVE_CYCLES" in med:
+                ratio.append(("wave cycles on VALU instructions / wave cycles",
+                              med["SQ_ACTIVE_INST_VALU"] / med["SQ_WAVE_CYCLES"]))
+            if ratio:
+                print("| derived | value |")
+                print("|---|---|")
+                for k_, v_ in ratio:
+                    print(f"| {k_} | {v_:.4g} |")
+                print()
+        return
     if kind == "l2":
         hits, misses = {}, {}
         for r in rows(paths[0], "*counter_collection.csv"):
@@ -673,7 +726,7 @@ def main():
     ap.add_argument("--configs", action="store_true", help="forward and backward on every named workload")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
-                         "'trace DIR [COUNT [SKIP]]', 'counters FETCH_DIR WRITE_DIR' or 'l2 DIR'")
+                         "'trace DIR [COUNT [SKIP]]', 'counters FETCH_DIR WRITE_DIR', 'l2 DIR' or 'pmc DIR...'")
     a = ap.parse_args()
     if a.summarize:
         summarize(a.summarize[0], a.summarize[1:])

@@ -104,3 +104,16 @@ def test_no_lds_write_or_smem_overwrite_during_lds_copies(tmp_path):
                 lines.append(ins)
     assert kernels >= 16, kernels
     assert not problems, problems
+
+
+def test_no_scratch_memory():
+    """Every kernel keeps its state in registers and LDS: no private
+    (scratch) memory and no spilled registers -- except the 256 x 128 tile of
+    the tile-size sweep, whose score and term registers do not fit beside the
+    accumulators (the sweep table reports its spills)."""
+    from tiled_exact_attention_fwd_amd.codeobj import kernel_resources
+    res = kernel_resources(LIB)
+    assert len(res) > 100
+    sweep_256x128 = "ELi8ELi128E"   # Fwd16<..., WQ = 8 waves, BKT = 128 keys>
+    bad = {n: r for n, r in res.items() if (r["scratch"] or r["vgpr_spill"]) and sweep_256x128 not in n}
+    assert not bad, bad

@@ -1040,8 +1040,7 @@ struct Fwd16P {
         const int tiles_q = pin_s(p.tiles_q);
         const int total = pin_s(p.total);
         unsigned long long* const counters = COUNT ? pin_s(p.counters) : nullptr;
-        // tile counts of the pairs processed: full, causal-masked, ragged, skipped
-        uint32_t n_full = 0, n_masked = 0, n_ragged = 0, n_skipped = 0;
+        uint32_t n_iter = 0;   // iterations that processed a (query tile, key tile) pair
 
         const int G = gridDim.x, b = blockIdx.x;
         // work units: query tiles, or (causal) pairs of query tiles; b < units
@@ -1159,7 +1158,7 @@ struct Fwd16P {
         uint32_t kc_ext = 0, vc_ext = 0;
         bool sm_on = false;                // this wave has rows in the softmax tile
 
-        auto iteration = [&](const int g, auto odd_tag) {
+        auto iteration = [&](const int g, auto odd_tag) __attribute__((always_inline)) {
             constexpr bool ODD = decltype(odd_tag)::value;
             uint8_t* kread = ODD ? kbuf0 : kbuf1;
             uint8_t* kfill = ODD ? kbuf1 : kbuf0;
@@ -1244,15 +1243,8 @@ struct Fwd16P {
                 vc_ext = head_bytes - vcopy;
             }
             if constexpr (COUNT) {
-                // the pair (query tile k0, key tile j0) whose softmax this
-                // iteration runs, classed as in add_tile_counts
-                if (j0 >= 0 && j0 < cur.nk && k0 < ntiles) {
-                    if (j0 == 0) n_skipped += (uint32_t)(nk_all - cur.nk);
-                    const int kk = j0 * BK;
-                    if (CAUSAL && kk + BK - 1 > cur.qt0) ++n_masked;
-                    else if (kk + BK > N) ++n_ragged;
-                    else ++n_full;
-                }
+                // this iteration's softmax runs on the pair (query tile k0, key tile j0)
+                if (j0 >= 0 && j0 < cur.nk && k0 < ntiles) ++n_iter;
             }
             st.meff = sm_on ? st.mc : __builtin_inff();
             st.lt = 0.f;
@@ -1313,12 +1305,31 @@ struct Fwd16P {
         // the last tile's output (its LSE was stored at the iteration g = gend)
         __syncthreads();
         store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
-        if (COUNT && tid == 0) {
-            atomicAdd(counters + 0, (unsigned long long)(n_full + n_masked + n_ragged));
-            atomicAdd(counters + 1, (unsigned long long)n_full);
-            atomicAdd(counters + 2, (unsigned long long)n_masked);
-            atomicAdd(counters + 3, (unsigned long long)n_ragged);
-            atomicAdd(counters + 4, (unsigned long long)n_skipped);
+        if constexpr (COUNT) {
+            // The pairs of the query tiles this workgroup processed, classed
+            // as in add_tile_counts: key tiles [0, nk) of each were visited,
+            // the rest of the head's key tiles skipped.  The computed count is
+            // the number of iterations that visited a pair; a decomposition
+            // that disagrees with the loop (the sum of nk over the tiles)
+            // shows as a computed count different from the classes' sum.
+            if (tid == 0) {
+                uint32_t full = 0, masked = 0, ragged = 0, skipped = 0;
+                for (int k = 0; k < ntiles; ++k) {
+                    const TileInfo t = decode(k);
+                    skipped += (uint32_t)(nk_all - t.nk);
+                    for (int j = 0; j < t.nk; ++j) {
+                        const int kk = j * BK;
+                        if (CAUSAL && kk + BK - 1 > t.qt0) ++masked;
+                        else if (kk + BK > N) ++ragged;
+                        else ++full;
+                    }
+                }
+                atomicAdd(counters + 0, (unsigned long long)n_iter);
+                atomicAdd(counters + 1, (unsigned long long)full);
+                atomicAdd(counters + 2, (unsigned long long)masked);
+                atomicAdd(counters + 3, (unsigned long long)ragged);
+                atomicAdd(counters + 4, (unsigned long long)skipped);
+            }
         }
     }
 };
