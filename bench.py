@@ -129,19 +129,19 @@ class ClockProbe:
         return res
 
 
-def window_summary(per, flops, mhz, cus):
-    """Per-launch durations of one bracketed window, the shader clock read by
-    probes right before its first and right after its last launch (mean over
-    64 CUs), and the matrix-core fraction at their mean."""
+def window_summary(per, probe_mhz):
+    """Per-launch durations of one bracketed window, and the rate of the
+    shader cycle counter that probes read right before its first and right
+    after its last launch (mean over 64 CUs).  The probes run after the load
+    has stopped: they read the clock the power manager has set, while inside
+    the matrix-core-bound kernel the same counter advances more slowly (the
+    chip's fast current limiter), so no fraction of a peak is derived from
+    them."""
     out = {"launch_ms": {"first": round(per[0], 5), "max": round(max(per), 5), "min": round(min(per), 5),
                          "mean": round(sum(per) / len(per), 5), "last": round(per[-1], 5)}}
-    if mhz and all(mhz):
-        clk = (mhz[0][0] + mhz[1][0]) / 2
-        peak = cus * 4096 * clk * 1e6 / 1e12
-        out["sclk_mhz"] = {"before": round(mhz[0][0], 1), "after": round(mhz[1][0], 1),
-                           "cu_range_after": [round(mhz[1][1], 1), round(mhz[1][2], 1)]}
-        out["mfma_peak_at_clock"] = round(peak, 1)
-        out["frac_at_clock"] = round(flops / (sum(per) / len(per) * 1e-3) / 1e12 / peak, 4)
+    if probe_mhz and all(probe_mhz):
+        out["cycle_counter_mhz"] = {"before": round(probe_mhz[0][0], 1), "after": round(probe_mhz[1][0], 1),
+                                    "cu_range_after": [round(probe_mhz[1][1], 1), round(probe_mhz[1][2], 1)]}
     return out
 
 
@@ -504,6 +504,12 @@ def summarize(kind, paths):
         # counters; per forward kernel the median over its dispatches, and
         # the ratios that locate its cycles
         vals = {}
+        agent = {"Num_Shader_Banks": 32, "Num_Xcc": 8, "Simd_Count": 1024}
+        for r in rows(paths[0], "*agent_info.csv"):
+            if r.get("Agent_Type") == "GPU":
+                agent = {k: int(r[k]) for k in agent}
+        print(f"agent: {agent}")
+        print()
         for d in paths:
             for r in rows(d, "*counter_collection.csv"):
                 if "fa::" not in r["Kernel_Name"]:
@@ -520,12 +526,20 @@ def summarize(kind, paths):
                 print(f"| {c} | {len(cs[c])} | {med[c]:.6g} |")
             print()
             ratio = []
+            # rocprofv3 sums each counter over its instances: SQ_CYCLES over the
+            # shader engines, GRBM_GUI_ACTIVE over the XCDs, the busy cycles
+            # over the SIMDs (the agent's Num_Shader_Banks, Num_Xcc, Simd_Count)
+            ses, xccs, simds = agent["Num_Shader_Banks"], agent["Num_Xcc"], agent["Simd_Count"]
             if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "SQ_CYCLES" in med:
-                ratio.append(("MFMA busy / SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / SQ_CYCLES)",
-                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_CYCLES"]))
+                ratio.append(("MFMA busy fraction of the dispatch's cycles (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / "
+                              "(SQ_CYCLES / shader engines))",
+                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (med["SQ_CYCLES"] / ses)))
             if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
-                ratio.append(("MFMA busy / (GRBM_GUI_ACTIVE x 1024 SIMDs)",
-                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * 1024)))
+                ratio.append(("the same against GRBM_GUI_ACTIVE / XCDs",
+                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (med["GRBM_GUI_ACTIVE"] / xccs)))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "SQ_INSTS_MFMA" in med:
+                ratio.append(("MFMA busy cycles per MFMA instruction",
+                              med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_INSTS_MFMA"]))
             if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
                 ratio.append(("matrix FLOPs (MOPS_BF16 x 512)", med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512))
             if "SQ_INSTS_MFMA" in med:
@@ -539,6 +553,10 @@ def summarize(kind, paths):
             if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
                 ratio.append(("LDS bank-conflict cycles / LDS active cycles",
                               med["SQ_LDS_BANK_CONFLICT"] / max(med["SQ_LDS_IDX_ACTIVE"], 1)))
+            if "SQ_ACTIVE_INST_VALU" in med and "SQ_CYCLES" in med:
+                ratio.append(("VALU-active fraction of a SIMD's cycles (SQ_ACTIVE_INST_VALU x 4 / SIMDs / "
+                              "(SQ_CYCLES / shader engines))",
+                              med["SQ_ACTIVE_INST_VALU"] * 4 / simds / (med["SQ_CYCLES"] / ses)))
             if "SQ_WAIT_INST_ANY" in med and "SQ_WAVE_CYCLES" in med:
                 ratio.append(("wave cycles waiting for an instruction's issue / wave cycles",
                               med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"]))
@@ -773,7 +791,6 @@ def main():
     # Every window's per-launch durations and average shader clock are in the
     # line, so each figure can be checked against them.
     probe = ClockProbe()
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
     wc, wl = W.WORKLOADS["C3"], W.WORKLOADS["C2b"]
     fw_causal, fw_head = prepare_forward(wc), prepare_forward(wl)
     bw_inputs = {key: prepare_backward(W.WORKLOADS[name], causal) for key, name, causal in BACKWARD_CASES}
@@ -814,14 +831,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic},
-        "window": window_summary(r["inside"], flops, r["sclk_mhz"], cus),
+        "window": window_summary(r["inside"], r["sclk_mhz"]),
         "order": ("inputs uploaded first; then back to back: backward, causal, headline (each: its warmup "
                   "launches, then its timed launches)"),
         "causal": {"workload": "same shape, causal, 1% of key rows x8",
                    "value": round(causal_value, 2), "unit": "TFLOP/s",
                    "ms_per_step": round(rc["ms_per_step"], 5),
                    "frac": round(causal_value / PEAK_TFLOPS["bf16"], 4),
-                   "window": window_summary(rc["inside"], fc, rc["sclk_mhz"], cus)},
+                   "window": window_summary(rc["inside"], rc["sclk_mhz"])},
         "backward": bwd,
         "cold_cache": cold,
         "settled_launch_ms": {"mean": round(r["launch_mean_ms"], 5), "median": round(r["launch_median_ms"], 5),
