@@ -193,10 +193,10 @@ int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k);
  * compute the expected counts for exactly that tiling (block counting of
  * §2.2 of "FlashAttention分块计算优化Transformer显存效率" at B_q = tile_q,
  * B_k = tile_k).  The choice depends on B * H, N, the mask, the output type
- * and the device's compute-unit count: 16-bit launches that fill the device
- * run persistent kernels (256 x 64 without a mask; 256 x 64 causal at
- * d = 128; 128 x 64 causal at d = 64), the others the per-tile kernels
- * (fa_fwd_tile_shape).  A launch with counters runs the instrumented
+ * and the device's compute-unit count: 16-bit launches at d = 128 that fill
+ * the device run persistent kernels (256 x 64 tiles under either mask), the
+ * others the per-tile kernels (fa_fwd_tile_shape: 256 x 64 without a mask
+ * and 128 x 64 causal at d = 128, 128 x 64 at d = 64, 64 x 64 in fp32).  A launch with counters runs the instrumented
  * instance of the kernel the same launch without counters runs.
  * Nothing is launched; args->counters is not read.  The arguments are
  * checked as by fa_fwd_ex (same error codes); then the device is queried

@@ -58,7 +58,8 @@ def test_build_info_and_strerror():
 def test_tile_shape():
     assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_F32, 64, 0) == (fa.FA_OK, 64, 64)
     assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 128, 1) == (fa.FA_OK, 128, 64)
-    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_F16, 64, 0) == (fa.FA_OK, 256, 64)
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_F16, 64, 0) == (fa.FA_OK, 128, 64)
+    assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 128, 0) == (fa.FA_OK, 256, 64)
     assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 96, 0)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_tile_shape(7, 64, 0)[0] == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_tile_shape(fa.FA_DTYPE_BF16, 64, 2)[0] == fa.FA_ERR_INVALID

@@ -283,27 +283,28 @@ def test_causal_tile_order_covers_every_tile(B, H, N, d):
 
 
 @pytest.mark.parametrize("dtype,B,H,N,d,scale,causal", [
-    ("bf16", 4, 80, 300, 64, None, False),     # 640 query tiles: 3 or 2 per workgroup; ragged rows and keys
-    ("f16", 2, 72, 520, 128, -0.3, False),     # 432 query tiles; last tile 8 rows; negative scale
+    ("f16", 2, 72, 520, 128, -0.3, False),     # 432 query tiles: 2 or 1 per workgroup; last tile 8 rows
     ("bf16", 1, 300, 1000, 128, None, False),  # 1200 query tiles, 16 key tiles each
     ("bf16", 1, 300, 200, 128, None, False),   # 4 key tiles (every iteration a transition), 1 query tile per head
-    ("f16", 3, 100, 330, 64, 0.2, False),      # 6 key tiles (one plain iteration per tile), 2 query tiles per head
-    ("bf16", 2, 300, 1000, 64, None, True),    # causal: 8 query tiles per head (2 .. 16 key tiles), 2400 pairs
+    ("bf16", 2, 130, 330, 128, 0.2, False),    # 6 key tiles (one plain iteration per tile), 2 query tiles per head
+    # d = 64: the per-tile kernel, three 128-row workgroups per CU, many rounds of them
+    ("bf16", 4, 80, 300, 64, None, False),     # 960 query tiles; ragged rows and keys
+    ("f16", 3, 100, 330, 64, 0.2, False),      # 900 query tiles; positive non-default scale
+    ("bf16", 2, 300, 1000, 64, None, True),    # causal: 8 query tiles per head (1 .. 16 key tiles)
     ("f16", 1, 600, 512, 64, -0.4, True),      # causal: 4 query tiles per head, negative scale
     ("bf16", 4, 50, 700, 64, None, True),      # causal: 6 query tiles, ragged last tile (rows and keys)
-    ("bf16", 1, 520, 256, 64, None, True),     # causal: one pair per head, tiles of 2 and 4 key tiles
     # causal at d = 128: 256-row query tiles in pairs (the diagonal over the last 4 key tiles)
     ("bf16", 4, 32, 2000, 128, None, True),    # 8 tiles per head, ragged last tile (208 rows), 512 pairs
     ("f16", 2, 160, 1024, 128, -0.3, True),    # 4 tiles per head (4 .. 16 key tiles), negative scale
     ("bf16", 1, 260, 512, 128, None, True),    # one pair per head: tiles of 4 and 8 key tiles
 ])
 def test_persistent_kernel(dtype, B, H, N, d, scale, causal):
-    """Plain launches with more query tiles than the device has workgroup
-    slots run the persistent kernel (without a mask; causal at d = 64 with
-    an even number of query tiles; causal at d = 128 with an even number of
-    256-row query tiles), which pipelines across query tiles; it
-    matches the oracle on every head, gives the same bits as the per-tile
-    kernel (the counters launch in launch_all), and repeats bit for bit."""
+    """Launches with more query tiles than the device has workgroup slots:
+    at d = 128 the persistent kernel (without a mask; causal with an even
+    number of 256-row query tiles), which pipelines across query tiles; at
+    d = 64 many rounds of the per-tile kernel.  Every head matches the oracle,
+    the instrumented instance gives the same bits and the tile counts (the
+    counters launch in launch_all), and launches repeat bit for bit."""
     words = W.make_words((B, H, N, d), dtype, "normal", seed=21)
     s = W.scale_for(d) if scale is None else scale
     _, (qd, kd, vd, o, lse, _) = check_against_oracle(words, dtype, causal, s, what="persistent")
@@ -313,8 +314,9 @@ def test_persistent_kernel(dtype, B, H, N, d, scale, causal):
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
 
 
-@pytest.mark.parametrize("shape,causal", [((2, 160, 1000, 64), False),   # persistent kernel
-                                          ((2, 300, 1000, 64), True),    # causal persistent kernel
+@pytest.mark.parametrize("shape,causal", [((2, 160, 1000, 128), False),  # persistent kernel
+                                          ((2, 128, 1024, 128), True),   # causal persistent kernel (pairs)
+                                          ((2, 300, 1000, 64), True),    # per-tile kernel, three per CU
                                           ((1, 8, 2048, 128), True)])    # per-tile kernel
 def test_graph_replay(shape, causal):
     """A launch captured into a HIP graph replays to the bits of the eager

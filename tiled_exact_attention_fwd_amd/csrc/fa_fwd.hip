@@ -38,7 +38,7 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 // Default tile shape per element type, head dimension and mask.
 void tile_shape(int dtype, int d, int causal, int* tq, int* tk) {
     if (dtype == FA_DTYPE_F32) { *tq = 64; *tk = 64; }
-    else { *tq = fa::tile_q16(causal != 0); *tk = 64; }
+    else { *tq = fa::tile_q16(causal != 0, d); *tk = 64; }
 }
 
 // The tile-size sweep shapes: bf16, d = 128, no mask, 16-bit output,
@@ -109,7 +109,7 @@ int check_device(int* cus) {
 // compute units; a launch with tile counters takes the same choice (the
 // instrumented instance of the same kernel), so its counts are those of the
 // kernel the plain launch runs.
-enum LaunchKind { kSweep, kPersistent, kPersistentCausalWide, kPersistentCausal, kPerTile16, kPerTile32 };
+enum LaunchKind { kSweep, kPersistent, kPersistentCausalWide, kPerTile16, kPerTile32 };
 struct LaunchPlan {
     LaunchKind kind;
     int tq, tk;     // query rows and keys of the tile the kernel works in
@@ -126,15 +126,17 @@ LaunchPlan plan_launch(const fa_fwd_args* a, int cus) {
     // kernel family)
     if (a->tile_q && sweep_shape(a, tq, tk)) return {kSweep, tq, tk, 0};
     const long long heads = (long long)a->B * a->H;
-    // A 16-bit launch without a mask that has more query tiles than the
-    // device has workgroup slots runs the persistent kernel: one workgroup
-    // per slot (a multiple of 8, so that each keeps to one XCD's tiles) takes
-    // every slots-th query tile and pipelines across them.
-    const int slots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(false);
+    // A 16-bit launch at d = 128 without a mask that has more query tiles
+    // than the device has CUs runs the persistent kernel: one workgroup per
+    // CU (a multiple of 8, so that each keeps to one XCD's tiles) takes every
+    // slots-th query tile and pipelines across them.  (At d = 64 three
+    // per-tile workgroups share a CU and keep it as busy; a persistent kernel
+    // with three workgroups per CU measured 1-2% either side of them.)
+    const int slots = cus / fa::kNumXcd * fa::kNumXcd;
     const int nk = (a->N + tk - 1) / tk;
     const long long tiles = heads * ((a->N + tq - 1) / tq);
-    if (!c && !o32 && slots > 0 && tiles > slots && nk >= fa::persistent_min_key_tiles())
-        return {kPersistent, tq, tk, slots};
+    if (!c && a->d == 128 && !o32 && slots > 0 && tiles > slots && nk >= fa::persistent_min_key_tiles())
+        return {kPersistent, fa::persistent_tile_q(), tk, slots};
     // Under the causal mask at d = 128: the persistent kernel with 256-row
     // query tiles (one workgroup per CU), each work unit a pair of query
     // tiles (i, T - 1 - i) of one head, whose key tiles add up to the same
@@ -145,16 +147,6 @@ LaunchPlan plan_launch(const fa_fwd_args* a, int cus) {
         if (wtiles % 2 == 0 && nk_first >= 4 && heads * wtiles / 2 > slots)
             return {kPersistentCausalWide, tw, tk, slots};
     }
-    // Likewise under the causal mask at d = 64, where two workgroups per CU
-    // fit their K, V, Q and output staging in LDS: each takes pairs of query
-    // tiles (i, T - 1 - i) of equal total cost, so T must be even.  Only for
-    // rows of at most 16 key tiles: measured 4% faster at N = 1000, but 1-3%
-    // slower from N = 2048 on, where the per-tile kernel's two co-resident
-    // workgroups already hide most of the per-tile cost.
-    const int cslots = cus / fa::kNumXcd * fa::kNumXcd * fa::resident16(true);
-    const int tiles_q = (a->N + tq - 1) / tq;
-    if (c && a->d == 64 && !o32 && cslots > 0 && tiles_q % 2 == 0 && tiles / 2 > cslots && nk <= 16)
-        return {kPersistentCausal, tq, tk, cslots};
     return {kPerTile16, tq, tk, 0};
 }
 
@@ -176,7 +168,7 @@ int run(const fa_fwd_args* a) {
     p.tiles_q = (a->N + plan.tq - 1) / plan.tq;
     p.heads = a->B * a->H;
     p.total = p.heads * p.tiles_q;
-    const int resident = a->dtype == FA_DTYPE_F32 ? fa::resident32() : fa::resident16(a->causal != 0);
+    const int resident = a->dtype == FA_DTYPE_F32 ? fa::resident32() : fa::resident16(a->causal != 0, a->d);
     p.group = fa::causal_group(p.heads, p.tiles_q, cus / fa::kNumXcd * resident);
     // softmax in base 2: exp(scale * s) = 2^(s * |scale| * log2 e) after a sign
     // flip of Q for negative scales; FLT_MIN keeps -inf * c at -inf for scale 0
@@ -205,16 +197,11 @@ int run(const fa_fwd_args* a) {
         default: return FA_ERR_UNSUPPORTED;
         }
     case kPersistent:
-        if (bf) return d64 ? fa::launch16p_bf16_d64(p, plan.grid, count, a->stream)
-                           : fa::launch16p_bf16_d128(p, plan.grid, count, a->stream);
-        return d64 ? fa::launch16p_f16_d64(p, plan.grid, count, a->stream)
-                   : fa::launch16p_f16_d128(p, plan.grid, count, a->stream);
+        return bf ? fa::launch16p_bf16_d128(p, plan.grid, count, a->stream)
+                  : fa::launch16p_f16_d128(p, plan.grid, count, a->stream);
     case kPersistentCausalWide:
         return bf ? fa::launch16pcw_bf16_d128(p, plan.grid, count, a->stream)
                   : fa::launch16pcw_f16_d128(p, plan.grid, count, a->stream);
-    case kPersistentCausal:
-        return bf ? fa::launch16pc_bf16_d64(p, plan.grid, count, a->stream)
-                  : fa::launch16pc_f16_d64(p, plan.grid, count, a->stream);
     case kPerTile16:
         if (bf) {
             if (d64) return c ? fa::launch16_bf16_d64_c1(p, o32, count, a->stream)
@@ -254,7 +241,7 @@ int run_split(const fa_fwd_args* a, float* o_part, float* lse_part, int splits) 
     if (a->out_dtype || a->counters || a->tile_q || a->tile_k) return FA_ERR_UNSUPPORTED;
     const bool causal = a->causal != 0;
     const bool f32 = a->dtype == FA_DTYPE_F32;
-    const int tq = f32 ? 64 : fa::tile_q16(causal), tk = 64;
+    const int tq = f32 ? 64 : fa::tile_q16(causal, a->d), tk = 64;
     // ranges of whole key tiles; as many as asked for, at most one per key tile
     const int nk = (a->N + tk - 1) / tk;
     const int per = (nk + std::min(splits, nk) - 1) / std::min(splits, nk);   // key tiles per range
@@ -377,8 +364,9 @@ const char* fa_strerror(int status) {
 
 const char* fa_build_info(void) {
     return "fa_fwd: offload-arch gfx950; flags: " FA_BUILD_FLAGS
-           "; kernels: bf16/f16 d64 and d128 (256x64 tiles non-causal, 128x64 causal, 32 query rows per wave; "
-           "persistent across query tiles without a mask), causal on/off, "
+           "; kernels: bf16/f16 d64 and d128 (d128: 256x64 tiles non-causal, 128x64 causal; d64: 128x64 tiles, "
+           "three workgroups per CU; 32 query rows per wave; d128 persistent across query tiles, causal in pairs "
+           "of 256-row tiles), causal on/off, "
            "out 16-bit/fp32, counters on/off; f32 d64/d128 (64x64 tiles), causal on/off, counters on/off; "
            "split-KV bf16/f16/f32 d64/d128 causal on/off (fp32 partials + merge); "
            "backward bf16/f16 d64/d128 causal on/off (dQ kernel, dK/dV kernel); "

@@ -23,7 +23,7 @@ namespace fa {
 int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
     using T = FA_TYPE(FA_INST_T);
     constexpr bool C = FA_INST_C != 0;
-    static_assert(Fwd16<T, FA_INST_D, C, true, true>::BQ == tile_q16(C), "grid tile");
+    static_assert(Fwd16<T, FA_INST_D, C, true, true>::BQ == tile_q16(C, FA_INST_D), "grid tile");
     if (out_f32)
         return count ? launch_kernel<Fwd16<T, FA_INST_D, C, true, true>>(p, stream)
                      : launch_kernel<Fwd16<T, FA_INST_D, C, true, false>>(p, stream);
@@ -35,7 +35,7 @@ int FA_NAME(const FwdParams& p, int out_f32, bool count, void* stream) {
 int FA_XCAT6(launch16s_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)(const FwdParams& p, void* o, float* lse,
                                                                    void* stream) {
     using K = Fwd16<FA_TYPE(FA_INST_T), FA_INST_D, FA_INST_C != 0, true, false, 0, 64, true>;
-    static_assert(K::BQ == tile_q16(FA_INST_C != 0) && K::BK == 64, "grid tile");
+    static_assert(K::BQ == tile_q16(FA_INST_C != 0, FA_INST_D) && K::BK == 64, "grid tile");
     void* args[] = {const_cast<FwdParams*>(&p)};
     hipError_t err = hipLaunchKernel((const void*)&fwd_kernel<K>, dim3(p.total * p.splits), dim3(K::NT), args, 0,
                                      (hipStream_t)stream);
@@ -50,12 +50,12 @@ int FA_XCAT6(launch16s_, FA_INST_T, _d, FA_INST_D, _c, FA_INST_C)(const FwdParam
 
 #define FA_CAT4(a, b, c, d) a##b##c##d
 #define FA_XCAT4(a, b, c, d) FA_CAT4(a, b, c, d)
-#if FA_INST_C == 0
+#if FA_INST_D == 128 && FA_INST_C == 0
 // the persistent kernel (no mask, 16-bit output) on `grid` workgroups; count:
 // its instrumented instance
 int FA_XCAT4(launch16p_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, bool count, void* stream) {
     using K = Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D>;
-    static_assert(K::BQ == tile_q16(false), "grid tile");
+    static_assert(K::BQ == persistent_tile_q(), "grid tile");
     return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D>>(p, stream, grid)
                  : launch_kernel<K>(p, stream, grid);
 }
@@ -66,14 +66,6 @@ int FA_XCAT4(launch16pcw_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int gri
     static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>::BQ == wide_tile_q(), "grid tile");
     return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid)
                  : launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true, true>>(p, stream, grid);
-}
-#else
-// the causal persistent kernel (d = 64, 16-bit output); count: its
-// instrumented instance
-int FA_XCAT4(launch16pc_, FA_INST_T, _d, FA_INST_D)(const FwdParams& p, int grid, bool count, void* stream) {
-    static_assert(Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>::BQ == tile_q16(true), "grid tile");
-    return count ? launch_kernel<Fwd16PCount<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid)
-                 : launch_kernel<Fwd16P<FA_TYPE(FA_INST_T), FA_INST_D, true>>(p, stream, grid);
 }
 #endif
 

@@ -12,7 +12,8 @@
 //
 // MI355X mapping (16-bit inputs):
 //   * One workgroup = one query tile of one (batch, head): 8 waves / 256 rows
-//     without a mask, 4 waves / 128 rows causal.  Each wave owns 32 query rows
+//     without a mask at d = 128, 4 waves / 128 rows causal (two workgroups
+//     per CU) and at d = 64 (three per CU).  Each wave owns 32 query rows
 //     for the whole key loop.
 //   * The scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 32 key scores of ONE
@@ -37,13 +38,12 @@
 //     one XCD (dispatch is round-robin over the 8 XCDs): the head's K and V
 //     are then re-read from that XCD's L2.  Causal launches issue query
 //     tiles longest first across all heads, which balances the CUs' loads.
-//   * Without a mask, launches with more query tiles than workgroup slots
-//     run a persistent variant (Fwd16P): one workgroup per CU runs the key
-//     loops of its query tiles back to back as one software pipeline, so the
+//   * At d = 128, launches with more query tiles than workgroup slots run a
+//     persistent variant (Fwd16P): one workgroup per CU runs the key loops
+//     of its query tiles back to back as one software pipeline, so the
 //     pipeline does not drain and refill between query tiles.  Under the
-//     mask the persistent variant takes pairs of query tiles (i, T - 1 - i)
-//     of equal total cost: with 256-row tiles at d = 128, with 128-row tiles
-//     (two workgroups per CU) at d = 64.
+//     mask the persistent variant takes pairs of 256-row query tiles
+//     (i, T - 1 - i) of equal total cost.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -306,14 +306,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <class T, int D, bool CAUSAL, bool OUT_F32, bool COUNT, int WQ = 0, int BKT = 64, bool SPLIT = false>
 struct Fwd16 {
     // Eight waves (256 query rows, one workgroup per CU) share each K / V
-    // tile copy without a mask: half the L2 -> LDS traffic of four.  Causal
-    // launches keep four waves (128 rows, two workgroups per CU): their
-    // waves' work differs along the diagonal, and a smaller workgroup waits
-    // less at its barriers for the wave with the most keys (under the
-    // longest-first tile order eight waves measure the same).
-    static constexpr int WAVES = WQ ? WQ : (CAUSAL ? 4 : 8);
+    // tile copy without a mask at d = 128: half the L2 -> LDS traffic of
+    // four.  Causal launches keep four waves (128 rows, two workgroups per
+    // CU): their waves' work differs along the diagonal, and a smaller
+    // workgroup waits less at its barriers for the wave with the most keys
+    // (under the longest-first tile order eight waves measure the same).  At
+    // d = 64 a wave needs about 165 registers, so three waves fit on a SIMD:
+    // four-wave workgroups, three per CU, under either mask -- a score costs
+    // half the matrix work of d = 128 but the same softmax work, and the third
+    // wave keeps more VALU work in flight beside the matrix cores.
+    static constexpr int WAVES = WQ ? WQ : (D == 64 || CAUSAL ? 4 : 8);
     static constexpr int BQ = 32 * WAVES;          // query rows per workgroup
-    static constexpr int OCC = 2;                  // waves per SIMD
+    static constexpr int OCC = D == 64 && WAVES == 4 ? 3 : 2;   // waves per SIMD
     static constexpr int RESIDENT = 4 * OCC / WAVES;   // workgroups per CU
     static constexpr int NT = 64 * WAVES;
     static constexpr int BK = BKT;                 // keys per tile
@@ -925,21 +929,16 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* opart, co
 // Without a mask the host uses it for nk >= 4, where these are four
 // different iterations.
 //
-// Causal variant (d = 64, two 128-row workgroups per CU): a query tile costs
-// its own number of key tiles, so a workgroup takes pairs of query tiles
-// (i, T - 1 - i) of a head, whose costs add up to the same for every pair.
-// The output has its own LDS slice, and the next tile's Q rows are copied
-// at j = 0, so that tiles of two key tiles (j = 0 and j = nk - 1 = 1) work;
-// the diagonal's masks fall on the last two key tiles of a query tile.
+// Causal variant (WIDE, d = 128): a query tile costs its own number of key
+// tiles, so a workgroup takes pairs of query tiles (i, T - 1 - i) of a head,
+// whose costs add up to the same for every pair.  With eight waves (256-row
+// query tiles, one workgroup per CU) every query tile has at least four key
+// tiles, so the transitions above apply unchanged, and the diagonal's masks
+// fall on the last four key tiles of a query tile.
 // ---------------------------------------------------------------------------
-// WIDE: the causal kernel with eight waves (256-row query tiles, one
-// workgroup per CU, d = 128): every query tile then has at least four key
-// tiles, so it uses the transitions of the kernel without a mask (no
-// separate output slice), and the diagonal's masks fall on the last four key
-// tiles of a query tile.
 template <class T, int D, bool CAUSAL = false, bool WIDE = false>
 struct Fwd16P {
-    using Bs = Fwd16<T, D, CAUSAL, false, false, WIDE ? 8 : 0>;
+    using Bs = Fwd16<T, D, CAUSAL, false, false, 8>;
     static constexpr int WAVES = Bs::WAVES, BQ = Bs::BQ, OCC = Bs::OCC, NT = Bs::NT, BK = Bs::BK;
     static constexpr int RESIDENT = Bs::RESIDENT;
     static constexpr int ROWB = Bs::ROWB, TILEB = Bs::TILEB, NS = Bs::NS, NDB = Bs::NDB, NMB = Bs::NMB;
@@ -948,20 +947,19 @@ struct Fwd16P {
     static constexpr bool READ_FIRST = Bs::READ_FIRST;
     static constexpr int SLICE = 32 * ROWB;          // one wave's Q / O staging bytes
     static constexpr int QLOADS = SLICE / 1024;      // 16-byte copies per lane of a wave's Q rows
-    static constexpr bool SPLIT = CAUSAL && !WIDE;   // the output has its own staging slice
-    static constexpr int MIN_KEY_TILES = SPLIT ? 2 : 4;
-    static constexpr int QCOPY_AT = SPLIT ? 0 : 2;   // key tile at which the next Q rows are copied
-    static constexpr int STEADY_LO = SPLIT ? 2 : 3;  // plain iterations: STEADY_LO <= j <= nk - 1 - TAIL
+    static constexpr int MIN_KEY_TILES = 4;
+    static constexpr int QCOPY_AT = 2;               // key tile at which the next Q rows are copied
+    static constexpr int STEADY_LO = 3;              // plain iterations: STEADY_LO <= j <= nk - 1 - TAIL
     // key tiles at the end of a query tile that are never plain: the K copy
     // of j + 2 crosses into the next tile from j = nk - 2 on, and under the
     // mask the diagonal covers the last BQ / BK key tiles
-    static constexpr int TAIL = CAUSAL && BQ / BK > 2 ? BQ / BK : 2;
+    static constexpr int TAIL = CAUSAL ? BQ / BK : 2;
     static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
     static constexpr int RPS = 64 / CPR;             // rows per 16-byte store
-    static_assert(SLICE % 1024 == 0 && RESIDENT == (SPLIT ? 2 : 1), "persistent shape");
-    static_assert(!WIDE || (CAUSAL && Bs::WAVES == 8), "wide causal shape");
-    static_assert((4 * TILEB + (SPLIT ? 2 : 1) * WAVES * SLICE) * RESIDENT <= 160 * 1024, "LDS per CU");
-    static_assert(!SPLIT || BQ == 2 * BK, "causal masks on the last two key tiles");
+    static_assert(SLICE % 1024 == 0 && RESIDENT == 1, "persistent shape");
+    static_assert(WIDE == CAUSAL && WAVES == 8, "the causal kernel has 256-row query tiles");
+    static_assert(!CAUSAL || BQ / BK > 2, "the diagonal's key tiles are never plain iterations");
+    static_assert(4 * TILEB + WAVES * SLICE <= 160 * 1024, "LDS per CU");
 
     // The lane index, opaque to the optimiser: addresses derived from it in a
     // once-per-tile block are computed there, not hoisted out of the key loop
@@ -1023,7 +1021,6 @@ struct Fwd16P {
         // places first: their operand reads keep addresses below 64 KiB,
         // which the 16-bit offset field of an LDS instruction can reach)
         __shared__ __attribute__((aligned(256))) uint8_t qbuf[WAVES * SLICE];
-        __shared__ __attribute__((aligned(256))) uint8_t obuf[SPLIT ? WAVES * SLICE : 16];
         const int tid = threadIdx.x;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lane = tid & 63;
@@ -1049,7 +1046,6 @@ struct Fwd16P {
         const int nk_all = (N + BK - 1) / BK;           // >= MIN_KEY_TILES
         const uint32_t head_bytes = (uint32_t)N * ROWB;
         uint8_t* const qslice = qbuf + wave * SLICE;
-        uint8_t* const oslice = SPLIT ? obuf + wave * SLICE : qslice;
 
         auto decode = [&](int k) {
             k = min(k, ntiles - 1);
@@ -1176,7 +1172,7 @@ struct Fwd16P {
                 }
                 if (j0 == 1 && k0 >= 1) {
                     // the previous tile's output (no copy of this wave in flight)
-                    store_output(acc, inv_prev, oslice, out, prv, wave, lane, N);
+                    store_output(acc, inv_prev, qslice, out, prv, wave, lane, N);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
                 }

@@ -9,15 +9,19 @@
 
 namespace fa {
 
-// Query rows per workgroup of the 16-bit kernels (the same for every
-// element type and head dimension); the host sizes the grid with it.
-constexpr int tile_q16(bool causal) {
-    return causal ? Fwd16<BF16, 128, true, false, false>::BQ : Fwd16<BF16, 128, false, false, false>::BQ;
+// Query rows per workgroup of the per-tile 16-bit kernels (the same for
+// both element types); the host sizes the grid with it.
+constexpr int tile_q16(bool causal, int d) {
+    return d == 64 ? (causal ? Fwd16<BF16, 64, true, false, false>::BQ : Fwd16<BF16, 64, false, false, false>::BQ)
+                   : (causal ? Fwd16<BF16, 128, true, false, false>::BQ : Fwd16<BF16, 128, false, false, false>::BQ);
 }
-// Workgroups of one kernel resident on a CU at a time (the causal tile
-// order groups heads by it)
-constexpr int resident16(bool causal) {
-    return causal ? Fwd16<BF16, 128, true, false, false>::RESIDENT : Fwd16<BF16, 128, false, false, false>::RESIDENT;
+// Workgroups of one per-tile kernel resident on a CU at a time (the causal
+// tile order groups heads by it)
+constexpr int resident16(bool causal, int d) {
+    return d == 64 ? (causal ? Fwd16<BF16, 64, true, false, false>::RESIDENT
+                             : Fwd16<BF16, 64, false, false, false>::RESIDENT)
+                   : (causal ? Fwd16<BF16, 128, true, false, false>::RESIDENT
+                             : Fwd16<BF16, 128, false, false, false>::RESIDENT);
 }
 constexpr int resident32() { return Fwd32<64, true, false>::RESIDENT; }
 
@@ -32,17 +36,13 @@ FA_DECLARE16(f16, 64, 1)
 FA_DECLARE16(f16, 128, 0)
 FA_DECLARE16(f16, 128, 1)
 #undef FA_DECLARE16
-// persistent kernels (no mask, 16-bit output; at least
-// persistent_min_key_tiles() key tiles), launched on `grid` workgroups;
-// count selects the instrumented instance
-int launch16p_bf16_d64(const FwdParams& p, int grid, bool count, void* stream);
+// persistent kernels (d = 128, no mask, 16-bit output; at least
+// persistent_min_key_tiles() key tiles), launched on `grid` workgroups (one
+// per CU); count selects the instrumented instance
 int launch16p_bf16_d128(const FwdParams& p, int grid, bool count, void* stream);
-int launch16p_f16_d64(const FwdParams& p, int grid, bool count, void* stream);
 int launch16p_f16_d128(const FwdParams& p, int grid, bool count, void* stream);
+constexpr int persistent_tile_q() { return Fwd16P<BF16, 128>::BQ; }
 constexpr int persistent_min_key_tiles() { return Fwd16P<BF16, 128>::MIN_KEY_TILES; }
-// causal persistent kernels (d = 64; an even number of query tiles, paired)
-int launch16pc_bf16_d64(const FwdParams& p, int grid, bool count, void* stream);
-int launch16pc_f16_d64(const FwdParams& p, int grid, bool count, void* stream);
 // causal persistent kernels with 256-row query tiles (d = 128; an even number
 // of query tiles, paired; every query tile at least 4 key tiles)
 constexpr int wide_tile_q() { return Fwd16P<BF16, 128, true, true>::BQ; }
