@@ -29,7 +29,14 @@ shape, non-causal and causal (after the copy kernel, for counter runs); the
 default line carries the same figures in its "backward" object.
 
 --configs times the forward (launch mean) and, for 16-bit inputs, the
-backward on every named workload, one JSON line each.
+backward on every named workload, one JSON line each, with the issue ceiling
+of the workload's head dimension (alu_peak: the matrix work and the softmax
+of the key loop co-issued on every SIMD, measured by the issue-rate probe of
+include/fa_probe.h at the start of the run) and the fraction of it reached
+(alu_frac).
+
+--issue-probe prints the probe's time per instruction per SIMD for each
+instruction mix of the key loop, and the ceilings they imply.
 
 --split times the split-KV forward (fa_fwd_split, 2-16 key ranges) against
 the plain launch on few-head long sequences (bf16, d = 128, non-causal and
@@ -241,6 +248,51 @@ def cold_cache(wl, reps=20):
             "how": "each launch timed alone after writing a 512 MiB buffer"}
 
 
+PROBE_MODES = [("v_exp_f32", 16), ("v_fma_f32", 16), ("v_add_f32", 16), ("v_cvt_pk_bf16_f32 (+xor)", 8),
+               ("softmax pair: 2 fma, 2 exp, 1 pack (+xor), 2 add", 4), ("v_mfma_f32_32x32x16_bf16", 4),
+               ("MFMA + 1 softmax pair (d = 64 ratio)", 4), ("MFMA + 1/2 softmax pair (d = 128 ratio)", 4)]
+
+
+def issue_probe(iters=20000):
+    """fa_issue_probe (include/fa_probe.h) over every mode: the chip-level
+    time per instruction (or per MFMA, or per softmax pair) per SIMD, and the
+    ceilings it implies.  The mixes hold no memory traffic, LDS reads or
+    barriers: what the VALU and the matrix cores sustain together, two waves
+    per SIMD, at the clock the chip holds under that load."""
+    import torch
+    import tiled_exact_attention_fwd_amd as fa
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    waves, simds = 8 * cus, 4 * cus
+    buf = torch.zeros(3 * waves, dtype=torch.int64, device="cuda")
+    tick_ns = 1e9 / (ClockProbe.attribute_khz(10017) * 1e3)
+    h = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for mode, (name, n) in enumerate(PROBE_MODES):
+        for _ in range(2):      # the first run settles the clock for this mix
+            st = fa.fa_issue_probe(mode, iters, buf.data_ptr(), buf.numel(), h)
+            if st != fa.FA_OK:
+                raise RuntimeError(f"fa_issue_probe: {fa.fa_strerror(st)}")
+        torch.cuda.synchronize()
+        v = buf.view(-1, 3).cpu()
+        wall_ns = (int(v[:, 2].max()) - int(v[:, 1].min())) * tick_ns
+        res[name] = wall_ns * simds / (waves * iters * n)
+    mfma = res["v_mfma_f32_32x32x16_bf16"]
+    flop = 2 * 32 * 32 * 16
+    out = {"ns_per_instruction_per_simd": {k: round(v_, 3) for k, v_ in res.items()},
+           "mfma_TFLOP/s": round(flop / mfma * simds / 1e3, 1),
+           "ceiling_TFLOP/s": {
+               "d64": round(flop / res["MFMA + 1 softmax pair (d = 64 ratio)"] * simds / 1e3, 1),
+               "d128": round(flop / res["MFMA + 1/2 softmax pair (d = 128 ratio)"] * simds / 1e3, 1)},
+           # the softmax alone: a pair instruction is 2 scores on each of 64 lanes, a score 4 d FLOPs
+           "softmax_only_TFLOP/s": {
+               "d64": round(128 * 4 * 64 / res["softmax pair: 2 fma, 2 exp, 1 pack (+xor), 2 add"] * simds / 1e3, 1),
+               "d128": round(128 * 4 * 128 / res["softmax pair: 2 fma, 2 exp, 1 pack (+xor), 2 add"] * simds / 1e3,
+                             1)},
+           "cus": cus}
+    return out
+
+
 def backward_flops(wl, causal):
     """10 B H N^2 d: the five N x N x d products of the backward (recomputed
     S, dP, dV, dK, dQ), 2.5 times the forward's convention, halved causal.
@@ -365,10 +417,14 @@ def split_kv(steps, warmup):
 
 def all_configs(steps, warmup):
     """Every named workload (C1-C5, each mask setting): forward time and
-    TFLOP/s with its fraction of the matching dense MFMA peak, and the
-    backward's time and TFLOP/s (10 B H N^2 d, halved causal).  One JSON line
-    per workload."""
+    TFLOP/s with its fraction of the matching dense MFMA peak, the issue
+    ceiling of its head dimension (the matrix work and the softmax of the key
+    loop co-issued, from the issue-rate probe, measured first) and its
+    fraction of it, and the backward's time and TFLOP/s (10 B H N^2 d, halved
+    causal).  One JSON line per workload."""
     import fa_workloads as W
+    probe = issue_probe()
+    print(json.dumps({"issue_probe": probe}), flush=True)
     for name, wl in W.WORKLOADS.items():
         for causal in wl.causal:
             r = time_workload(wl, causal, steps, warmup)
@@ -377,6 +433,8 @@ def all_configs(steps, warmup):
             row = {"workload": name, "shape": list(wl.shape), "dtype": wl.dtype, "values": wl.values,
                    "causal": causal, "fwd_us": round(r["launch_mean_ms"] * 1e3, 1), "fwd_TFLOP/s": round(tf, 1),
                    "fwd_frac": round(tf / PEAK_TFLOPS[wl.dtype], 4),
+                   "alu_peak": probe["ceiling_TFLOP/s"][f"d{wl.d}"] if wl.dtype != "f32" else None,
+                   "alu_frac": round(tf / probe["ceiling_TFLOP/s"][f"d{wl.d}"], 4) if wl.dtype != "f32" else None,
                    "hbm_min_GB/s": round((4 * wl.B * wl.H * wl.N * wl.d * (4 if wl.dtype == "f32" else 2)
                                           + 4 * wl.B * wl.H * wl.N) / (r["launch_mean_ms"] * 1e-3) / 1e9, 1)}
             ms = time_backward(wl, causal, max(5, steps // 4), max(3, warmup // 4))
@@ -742,6 +800,7 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time only the backward pass (fa_bwd)")
     ap.add_argument("--split", action="store_true", help="split-KV forward against the plain one, few heads")
     ap.add_argument("--configs", action="store_true", help="forward and backward on every named workload")
+    ap.add_argument("--issue-probe", action="store_true", help="issue rates of the key loop's instruction mixes")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a profiles/ summary of rocprofv3 csv output: "
                          "'trace DIR [COUNT [SKIP]]', 'counters FETCH_DIR WRITE_DIR', 'l2 DIR' or 'pmc DIR...'")
@@ -775,6 +834,9 @@ def main():
         return
     if a.configs:
         all_configs(a.steps, a.warmup)
+        return
+    if a.issue_probe:
+        print(json.dumps({"issue_probe": issue_probe()}), flush=True)
         return
     if a.backward:
         copy_calibration()

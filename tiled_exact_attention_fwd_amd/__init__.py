@@ -62,6 +62,7 @@ SIGNATURES = {
     "fa_bwd": (_I, _BWD17 + [_I]),
     "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _I]),
     "fa_clock_probe": (_I, [_P, ctypes.c_uint, _P]),
+    "fa_issue_probe": (_I, [_I, _I, _P, ctypes.c_longlong, _P]),
 }
 FA_ERR_SCRATCH = 4
 BWD_NOALLOC_MAX_ROWS = 1 << 22
@@ -251,6 +252,10 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
 
 def fa_clock_probe(out, ticks, stream):
     return lib().fa_clock_probe(out, ticks, stream)
+
+
+def fa_issue_probe(mode, iters, out, out_len, stream):
+    return lib().fa_issue_probe(mode, iters, out, out_len, stream)
 
 
 def fa_fwd_tile_shape(dtype, d, causal):
