@@ -114,11 +114,11 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     const bool c = causal != 0;
     int rc;
     if (dtype == FA_DTYPE_BF16)
-        rc = d == 64 ? fa::bwd::launch_bwd_bf16_d64(p, (int)heads, c, stream)
-                     : fa::bwd::launch_bwd_bf16_d128(p, (int)heads, c, stream);
+        rc = d == 64 ? fa::bwd::launch_bwd_bf16_d64(p, (int)heads, cus, c, stream)
+                     : fa::bwd::launch_bwd_bf16_d128(p, (int)heads, cus, c, stream);
     else
-        rc = d == 64 ? fa::bwd::launch_bwd_f16_d64(p, (int)heads, c, stream)
-                     : fa::bwd::launch_bwd_f16_d128(p, (int)heads, c, stream);
+        rc = d == 64 ? fa::bwd::launch_bwd_f16_d64(p, (int)heads, cus, c, stream)
+                     : fa::bwd::launch_bwd_f16_d128(p, (int)heads, cus, c, stream);
     return rc == 0 ? FA_OK : FA_ERR_HIP;
 }
 

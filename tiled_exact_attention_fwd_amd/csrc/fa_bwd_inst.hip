@@ -22,10 +22,14 @@ struct bf16 { using T = BF16; };
 struct f16 { using T = F16; };
 
 template <class T, int D, bool C>
-int launch(const BwdParams& p0, int heads, void* stream) {
+int launch(const BwdParams& p0, int heads, int cus, void* stream) {
     BwdParams p = p0;
     p.nblk = (p.N + DqShape<D>::ROWS - 1) / DqShape<D>::ROWS;
     p.nblk_k = (p.N + DkdvShape<D>::KEYS - 1) / DkdvShape<D>::KEYS;
+    // causal: heads per group as in the forward (a group's blocks fill the
+    // XCD's workgroup slots twice)
+    p.group = causal_group(heads, p.nblk, cus / kNumXcd * DqShape<D>::PER_CU);
+    p.group_k = causal_group(heads, p.nblk_k, cus / kNumXcd * DkdvShape<D>::PER_CU);
     const hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL((dq_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk)), dim3(DqShape<D>::NT), 0, st, p);
     hipLaunchKernelGGL((dkdv_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk_k)), dim3(DkdvShape<D>::NT), 0, st, p);
@@ -33,9 +37,10 @@ int launch(const BwdParams& p0, int heads, void* stream) {
 }
 }  // namespace
 
-int FA_NAME(const BwdParams& p, int heads, bool causal, void* stream) {
+int FA_NAME(const BwdParams& p, int heads, int cus, bool causal, void* stream) {
     using T = FA_INST_T::T;
-    return causal ? launch<T, FA_INST_D, true>(p, heads, stream) : launch<T, FA_INST_D, false>(p, heads, stream);
+    return causal ? launch<T, FA_INST_D, true>(p, heads, cus, stream)
+                  : launch<T, FA_INST_D, false>(p, heads, cus, stream);
 }
 
 }  // namespace bwd

@@ -62,6 +62,8 @@ struct BwdParams {
     int heads;     // B * H
     int nblk;      // query blocks per head (dq_kernel, DqShape<D>::ROWS rows each)
     int nblk_k;    // key blocks per head (dkdv_kernel, DkdvShape<D>::KEYS keys each)
+    int group;     // causal: heads per group of dq_kernel's block order
+    int group_k;   // causal: heads per group of dkdv_kernel's block order
     float c;       // scale * log2(e)
     float scale;
 };
@@ -129,15 +131,19 @@ __device__ __forceinline__ u32x4_t tr_operand(const uint8_t* lds, int blk, int t
 }
 
 // Causal launches: workgroup -> (head, rank), where rank 0 is a head's most
-// expensive block.  Blocks are issued rank-major so that the launch ends with
-// the cheap ones; with a head count divisible by 8, XCD x (which runs
-// workgroups b = x mod 8) owns heads x, x + 8, ... and takes their blocks
-// rank-major, so that a head's tiles stay on one XCD's L2.
-__device__ __forceinline__ void causal_order(int bid, int heads, int& hh, int& rank) {
+// expensive block.  With a head count divisible by 8, XCD x (which runs
+// workgroups b = x mod 8) owns heads x, x + 8, ... and takes them in groups
+// of `group` heads, one group after the other, rank-major inside a group:
+// the launch ends with the cheap blocks of the last group, and the K / V (or
+// Q / dO) tiles re-read by a group's blocks stay in the XCD's L2 while the
+// group runs.  The last group of an XCD may hold fewer heads.
+__device__ __forceinline__ void causal_order(int bid, int heads, int nblk, int group, int& hh, int& rank) {
     if (heads % kNumXcd == 0) {
         const int x = bid % kNumXcd, s = bid / kNumXcd, hpx = heads / kNumXcd;
-        rank = s / hpx;
-        hh = (s - rank * hpx) * kNumXcd + x;
+        const int gi = s / (group * nblk), r = s - gi * group * nblk;
+        const int g = min(group, hpx - gi * group);
+        rank = r / g;
+        hh = (gi * group + r - rank * g) * kNumXcd + x;
     } else {
         rank = bid / heads;
         hh = bid - rank * heads;
@@ -177,6 +183,7 @@ struct DqShape {
     static constexpr int WAVES = D == 128 ? 8 : 4;
     static constexpr int NT = 64 * WAVES;
     static constexpr int ROWS = 32 * WAVES;
+    static constexpr int PER_CU = D == 128 ? 1 : 3;    // resident workgroups per CU
 };
 
 template <class T, int D, bool CAUSAL>
@@ -192,7 +199,7 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kern
     const int N = p.N;
     int hh, qb;
     if (CAUSAL) {
-        causal_order(blockIdx.x, p.heads, hh, qb);
+        causal_order(blockIdx.x, p.heads, p.nblk, p.group, hh, qb);
         qb = p.nblk - 1 - qb;                  // the last rows see the most keys
     } else {
         const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -292,6 +299,7 @@ struct DkdvShape {
     static constexpr int NT = 64 * WAVES;
     static constexpr int KEYS = 32 * WAVES;        // keys per workgroup
     static constexpr bool V_LDS = D == 128;
+    static constexpr int PER_CU = D == 128 ? 1 : 2;    // resident workgroups per CU
 };
 
 template <class T, int D, bool CAUSAL>
@@ -311,7 +319,7 @@ dkdv_kernel(BwdParams p) {
     const int N = p.N;
     int hh, kb;                                // causal: block 0 sees the most queries
     if (CAUSAL) {
-        causal_order(blockIdx.x, p.heads, hh, kb);
+        causal_order(blockIdx.x, p.heads, p.nblk_k, p.group_k, hh, kb);
     } else {
         const int L = xcd_remap(blockIdx.x, gridDim.x);
         hh = L / p.nblk_k;
