@@ -71,6 +71,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int dtype);
 
 /*
+ * fa_bwd with O in fp32: o is a dense row-major [B, H, N, d] fp32 array (the
+ * forward's fp32 output, fa_fwd_ex with out_dtype = 1) whatever dtype says;
+ * every other argument, the layout of the rest and the errors are those of
+ * fa_bwd.  O enters the backward only through D[i] = sum_c dO[i,c] O[i,c]
+ * (the identity D[i] = sum_j P[i,j] dP[i,j] above, which holds for the exact
+ * O); from a 16-bit O, D carries that O's rounding (relative 2^-9 in bf16 per
+ * element), and dS = P * (dP - D) magnifies it wherever dP - D is small.
+ * From the fp32 O, D is as accurate as the forward's fp32 accumulators.
+ * With o holding exactly the values of a 16-bit O the result equals
+ * fa_bwd's bit for bit.  dtype FA_DTYPE_F32 is fa_bwd itself.
+ */
+int fa_bwd_o32(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream, int dtype);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd
  * without the delta argument.  The D work array lives in a fixed scratch

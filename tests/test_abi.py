@@ -211,6 +211,33 @@ def test_backward_argument_checks():
         assert fn(Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 1, 1, 48, 1.0, 0, None) == fa.FA_ERR_UNSUPPORTED
 
 
+def test_backward_o32_argument_checks():
+    """fa_bwd_o32: fa_bwd's checks, with o taken as fp32 (4-byte elements)
+    whatever the element type of the rest."""
+    DO, DQ, DK, DV, DL = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+    def bwd(**over):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, H=3, N=100, d=64,
+                 scale=0.125, causal=0, stream=None, dtype=fa.FA_DTYPE_BF16)
+        a.update(over)
+        return fa.fa_bwd_o32(**a)
+    for field in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta"):
+        assert bwd(**{field: None}) == fa.FA_ERR_INVALID
+    assert bwd(B=0) == fa.FA_ERR_INVALID
+    assert bwd(causal=2) == fa.FA_ERR_INVALID
+    assert bwd(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(dtype=9) == fa.FA_ERR_UNSUPPORTED
+    n16 = 2 * 3 * 100 * 64 * 2
+    # an output just past a 16-bit O lies inside the fp32 one
+    assert bwd(dq=O + n16) == fa.FA_ERR_INVALID
+    assert bwd(dq=O + 2 * n16 - 4) == fa.FA_ERR_INVALID
+    if NO_GPU:
+        assert bwd(dq=O + 2 * n16) in (fa.FA_ERR_HIP, fa.FA_OK)
+        assert fa.fa_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=O + n16, dk=DK, dv=DV, delta=DL, B=2, H=3,
+                         N=100, d=64, scale=0.125, causal=0, stream=None,
+                         dtype=fa.FA_DTYPE_BF16) in (fa.FA_ERR_HIP, fa.FA_OK)
+
+
 def test_backward_noalloc_argument_checks():
     """fa_bwd_noalloc: fa_bwd's checks without the delta argument, and a
     problem beyond its fixed scratch array (one fp32 per query row) refused

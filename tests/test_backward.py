@@ -152,6 +152,60 @@ def test_entry_points_agree():
     assert torch.allclose(delta, ref, atol=1e-4, rtol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_o32_equals_o16_bits(dtype, d, causal):
+    """fa_bwd_o32 handed the 16-bit O widened to fp32 takes the same D, so
+    it returns fa_bwd's bits."""
+    print(f"backward o32 bits {dtype} d={d} causal={causal}", flush=True)
+    words, dwords = inputs((2, 3, 700, d), dtype, "normal", 21)
+    (qd, kd, vd, dod, o, lse), a = run_device(words, dwords, dtype, causal, W.scale_for(d))
+    b = fa.attention_backward(qd, kd, vd, o.float(), lse, dod, causal=causal, scale=W.scale_for(d))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x.view(torch.int16),
+                           y.view(torch.int32) if y.dtype == torch.float32 else y.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_o32_accuracy(dtype):
+    """D from the forward's fp32 O (fa_bwd_o32): within the gate on spiky
+    causal heads, and no less accurate than D from the 16-bit O; D itself
+    within fp32 rounding of the oracle's D from the exact O."""
+    print(f"backward o32 accuracy {dtype}", flush=True)
+    words, dwords = inputs((1, 4, 1536, 128), dtype, "spiky", 23)
+    scale = W.scale_for(128)
+    qd, kd, vd = (to_dev(w, dtype) for w in words)
+    dod = to_dev(dwords, dtype)
+    o16, lse = fa.attention(qd, kd, vd, causal=True, scale=scale)
+    o32, lse32 = fa.attention(qd, kd, vd, causal=True, scale=scale, out_f32=True)
+    r16 = fa.attention_backward(qd, kd, vd, o16, lse, dod, causal=True, scale=scale)
+    r32 = fa.attention_backward(qd, kd, vd, o32, lse32, dod, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    B, H, N, d = words[0].shape
+    vals = [np.stack([W.decode64(w[0, h], dtype) for h in range(H)])[:, None] for w in (*words, dwords)]
+    ref = oracle.attention_bwd_ref(*vals, scale, True)
+    e = {}
+    for tag, r in (("o16", r16), ("o32", r32)):
+        dev = [out_to64(t)[0][:, None] for t in r[:3]]
+        e[tag] = grad_errors(dev, ref, dtype)
+    print(e)
+    assert max(e["o32"].values()) <= TOL[dtype], e
+    for name in ("dq", "dk", "dv"):
+        assert e["o32"][name] <= e["o16"][name] * 1.05 + 1e-4, e
+    # D = rowsum(dO * O) against the exact O (float64, the oracle's forward):
+    # the fp32 O carries only the forward's rounding of each weight P to 16
+    # bits (relative 2^-8 at most for bf16, so |dO_c| * 2^-8 * max_j |V_jc|
+    # per column), not the 16-bit rounding of O itself
+    o_ref, _ = oracle.attention_ref(vals[0], vals[1], vals[2], scale, True)
+    d_ref = (vals[3] * o_ref).sum(axis=-1)[:, 0]
+    d_dev = r32[3][0].double().cpu().numpy()
+    vmax = np.abs(vals[2]).max(axis=2, keepdims=True)
+    bound = 2.0 ** -8 * (np.abs(vals[3]) * vmax).sum(axis=-1)[:, 0] + 1e-30
+    assert np.all(np.abs(d_dev - d_ref) <= bound), float(np.max(np.abs(d_dev - d_ref) / bound))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_graph_replay(causal):
     """The backward's two launches captured into a HIP graph replay to the
@@ -228,7 +282,11 @@ def test_long_context_sampled_rows():
     words, dwords = inputs(wl.shape, wl.dtype, wl.values, W.default_seed())
     B, H, N, d = wl.shape
     scale = W.scale_for(d)
-    _, (dq, dk, dv, _) = run_device(words, dwords, wl.dtype, True, scale)
+    (qd, kd, vd, dod, _, _), (dq, dk, dv, _) = run_device(words, dwords, wl.dtype, True, scale)
+    # and the same with D from the forward's fp32 O (fa_bwd_o32)
+    o32, lse32 = fa.attention(qd, kd, vd, causal=True, scale=scale, out_f32=True)
+    dq32, dk32, dv32, _ = fa.attention_backward(qd, kd, vd, o32, lse32, dod, causal=True, scale=scale)
+    torch.cuda.synchronize()
     rng = np.random.default_rng(77)
     qr = np.arange(N)
     kr = sample_rows(N, 256, rng, n_random=16, cap=24)
@@ -237,8 +295,11 @@ def test_long_context_sampled_rows():
     ref = oracle.attention_bwd_sampled(*vals, scale, True, qr, kr, chunk=1024)
     dev = [out_to64(dq[b, h, qr]), out_to64(dk[b, h, kr]), out_to64(dv[b, h, kr])]
     errs = grad_errors(dev, ref, wl.dtype)
-    print("long context", errs)
+    dev32 = [out_to64(dq32[b, h, qr]), out_to64(dk32[b, h, kr]), out_to64(dv32[b, h, kr])]
+    errs32 = grad_errors(dev32, ref, wl.dtype)
+    print("long context", errs, "with the fp32 O", errs32)
     assert max(errs.values()) <= TOL[wl.dtype], errs
+    assert max(errs32.values()) <= TOL[wl.dtype], errs32
     colsum = dk.float().sum(dim=2).abs().max().item()
     assert colsum <= TOL[wl.dtype] * dk.float().abs().max().item() * N ** 0.5
 

@@ -60,6 +60,7 @@ SIGNATURES = {
     "fa_bwd_f16": (_I, _BWD17),
     "fa_bwd_f32": (_I, _BWD17),
     "fa_bwd": (_I, _BWD17 + [_I]),
+    "fa_bwd_o32": (_I, _BWD17 + [_I]),
     "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _P, _I]),
     "fa_clock_probe": (_I, [_P, ctypes.c_uint, _P]),
     "fa_issue_probe": (_I, [_I, _I, _P, ctypes.c_longlong, _P]),
@@ -211,6 +212,10 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, 
     return lib().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype)
 
 
+def fa_bwd_o32(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype):
+    return lib().fa_bwd_o32(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype)
+
+
 def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream, dtype):
     return lib().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream, dtype)
 
@@ -219,13 +224,16 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
     """Gradients ``(dq, dk, dv)`` of the attention forward on the device
     (include/fa_bwd.h), from the forward's ``o`` and ``lse`` for the same
     inputs and the output gradient ``dout`` ([B, H, N, d] tensors of one
-    type, bf16, fp16 or fp32; lse [B, H, N] fp32).  Also returns the ``delta`` work array the call
-    wrote (rowsum(dout * o), fp32)."""
+    type, bf16, fp16 or fp32; lse [B, H, N] fp32).  ``o`` may also be the
+    forward's fp32 output (``attention(..., out_f32=True)``) for 16-bit
+    inputs: D = rowsum(dout * o) is then taken from it (``fa_bwd_o32``).
+    Also returns the ``delta`` work array the call wrote (D, fp32)."""
     import math
     import torch
     ts = (q, k, v, o, dout)
-    if not all(t.dtype == q.dtype for t in ts):
-        raise ValueError("q, k, v, o, dout must share one dtype")
+    o32 = o.dtype == torch.float32 and q.dtype != torch.float32
+    if not all(t.dtype == q.dtype for t in (q, k, v, dout)) or not (o32 or o.dtype == q.dtype):
+        raise ValueError("q, k, v, dout must share one dtype, and o that one or fp32")
     if q.dim() != 4 or not all(t.shape == q.shape for t in ts):
         raise ValueError("q, k, v, o, dout must all be [B, H, N, d]")
     for t in ts + (lse,):
@@ -240,13 +248,15 @@ def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=N
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
-                int(bool(causal)), stream, dtype_code(q.dtype))
+    entry = fa_bwd_o32 if o32 else fa_bwd
+    st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
+               int(bool(causal)), stream, dtype_code(q.dtype))
+    name = "fa_bwd_o32" if o32 else "fa_bwd"
     if st == FA_ERR_INVALID:
-        raise ValueError(f"fa_bwd: {fa_strerror(st)}")
+        raise ValueError(f"{name}: {fa_strerror(st)}")
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, name)
     return dq, dk, dv, delta
 
 

@@ -57,8 +57,9 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 
 int run(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
         void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
-        int dtype, bool noalloc = false) {
-    // noalloc: delta is ignored and the D array lives in `scratch`
+        int dtype, bool noalloc = false, bool o32 = false) {
+    // noalloc: delta is ignored and the D array lives in `scratch`;
+    // o32: o is fp32 whatever the element type
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (!noalloc && !delta)) return FA_ERR_INVALID;
     if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID;
@@ -71,9 +72,9 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     if ((uint64_t)N * d * 4 >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
     const uint64_t heads = (uint64_t)B * H, nblk = ((uint64_t)N + 127) / 128;
     if (heads * nblk >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
-    const uint64_t tb = heads * N * d * e, sb = heads * N * 4;
+    const uint64_t tb = heads * N * d * e, sb = heads * N * 4, ob = o32 ? heads * N * d * 4 : tb;
     const void* ins[6] = {q, k, v, o, dout, lse};
-    const uint64_t inb[6] = {tb, tb, tb, tb, tb, sb};
+    const uint64_t inb[6] = {tb, tb, tb, ob, tb, sb};
     void* outs[4] = {dq, dk, dv, delta};
     const uint64_t outb[4] = {tb, tb, tb, sb};
     const int nouts = noalloc ? 3 : 4;
@@ -104,7 +105,8 @@ int run(const void* q, const void* k, const void* v, const void* o, const float*
     }
     fa::bwd::BwdParams p;
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
-    p.o = (const uint16_t*)o; p.dout = (const uint16_t*)dout; p.lse = lse;
+    p.o = o32 ? nullptr : (const uint16_t*)o; p.o32 = o32 ? (const float*)o : nullptr;
+    p.dout = (const uint16_t*)dout; p.lse = lse;
     p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv; p.delta = delta;
     p.N = N;
     p.heads = (int)heads;
@@ -130,6 +132,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, void* stream,
            int dtype) {
     return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype);
+}
+
+int fa_bwd_o32(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+               void* stream, int dtype) {
+    return run(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype, false, true);
 }
 
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -21,7 +21,7 @@ namespace {
 struct bf16 { using T = BF16; };
 struct f16 { using T = F16; };
 
-template <class T, int D, bool C>
+template <class T, int D, bool C, bool O32>
 int launch(const BwdParams& p0, int heads, int cus, void* stream) {
     BwdParams p = p0;
     p.nblk = (p.N + DqShape<D>::ROWS - 1) / DqShape<D>::ROWS;
@@ -31,7 +31,7 @@ int launch(const BwdParams& p0, int heads, int cus, void* stream) {
     p.group = causal_group(heads, p.nblk, cus / kNumXcd * DqShape<D>::PER_CU);
     p.group_k = causal_group(heads, p.nblk_k, cus / kNumXcd * DkdvShape<D>::PER_CU);
     const hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL((dq_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk)), dim3(DqShape<D>::NT), 0, st, p);
+    hipLaunchKernelGGL((dq_kernel<T, D, C, O32>), dim3((unsigned)(heads * p.nblk)), dim3(DqShape<D>::NT), 0, st, p);
     hipLaunchKernelGGL((dkdv_kernel<T, D, C>), dim3((unsigned)(heads * p.nblk_k)), dim3(DkdvShape<D>::NT), 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -39,8 +39,11 @@ int launch(const BwdParams& p0, int heads, int cus, void* stream) {
 
 int FA_NAME(const BwdParams& p, int heads, int cus, bool causal, void* stream) {
     using T = FA_INST_T::T;
-    return causal ? launch<T, FA_INST_D, true>(p, heads, cus, stream)
-                  : launch<T, FA_INST_D, false>(p, heads, cus, stream);
+    if (p.o32)
+        return causal ? launch<T, FA_INST_D, true, true>(p, heads, cus, stream)
+                      : launch<T, FA_INST_D, false, true>(p, heads, cus, stream);
+    return causal ? launch<T, FA_INST_D, true, false>(p, heads, cus, stream)
+                  : launch<T, FA_INST_D, false, false>(p, heads, cus, stream);
 }
 
 }  // namespace bwd

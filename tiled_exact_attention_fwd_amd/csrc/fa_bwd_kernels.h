@@ -55,6 +55,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
+    const float* o32;  // O in fp32 (dq_kernel<.., O32 = true>; o unused then)
     const float* lse;
     uint16_t *dq, *dk, *dv;
     float* delta;
@@ -81,6 +82,19 @@ template <class T> __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
     for (int i = 0; i < 4; ++i) {
         s += to_f32<T>(a[i] & 0xffffu) * to_f32<T>(b[i] & 0xffffu);
         s += to_f32<T>(a[i] >> 16) * to_f32<T>(b[i] >> 16);
+    }
+    return s;
+}
+
+// the same with the second vector in fp32 (elements 0..3 in lo, 4..7 in hi),
+// summed in the same order: equal bits when it holds the 16-bit values
+template <class T> __device__ __forceinline__ float dot8f(u32x4_t a, u32x4_t lo, u32x4_t hi) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b0 = i < 2 ? lo[2 * i] : hi[2 * i - 4], b1 = i < 2 ? lo[2 * i + 1] : hi[2 * i - 3];
+        s += to_f32<T>(a[i] & 0xffffu) * __uint_as_float(b0);
+        s += to_f32<T>(a[i] >> 16) * __uint_as_float(b1);
     }
     return s;
 }
@@ -186,7 +200,8 @@ struct DqShape {
     static constexpr int PER_CU = D == 128 ? 1 : 3;    // resident workgroups per CU
 };
 
-template <class T, int D, bool CAUSAL>
+// O32: D = rowsum(dO * O) from an fp32 O (p.o32) instead of the 16-bit one
+template <class T, int D, bool CAUSAL, bool O32 = false>
 __global__ void __launch_bounds__(DqShape<D>::NT)
 __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kernel(BwdParams p) {
     using G = Geo<D>;
@@ -210,7 +225,8 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kern
     const size_t head = (size_t)hh * N * D;
     const uint32_t hb = (uint32_t)N * D * 2;
     const auto rq = make_rsrc(p.q + head, hb), rk = make_rsrc(p.k + head, hb), rv = make_rsrc(p.v + head, hb);
-    const auto ro = make_rsrc(p.o + head, hb), rdo = make_rsrc(p.dout + head, hb);
+    const auto rdo = make_rsrc(p.dout + head, hb);
+    const auto ro = O32 ? make_rsrc(p.o32 + head, 2 * hb) : make_rsrc(p.o + head, hb);
 
     // the wave's rows as B operands: lane (li, lh) holds row q, columns 16 s + 8 lh .. +7
     u32x4_t qreg[G::NS], dreg[G::NS];
@@ -220,7 +236,10 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kern
         const uint32_t off = (uint32_t)((q * D + 16 * s + 8 * lh) * 2);
         qreg[s] = buf_load16(rq, off);
         dreg[s] = buf_load16(rdo, off);
-        dsum += dot8<T>(dreg[s], buf_load16(ro, off));
+        if constexpr (O32)
+            dsum += dot8f<T>(dreg[s], buf_load16(ro, 2 * off), buf_load16(ro, 2 * off + 16));
+        else
+            dsum += dot8<T>(dreg[s], buf_load16(ro, off));
     }
     dsum = sum_halves(dsum);
     const bool qok = q < N;
