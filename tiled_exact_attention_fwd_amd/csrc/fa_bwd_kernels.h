@@ -388,18 +388,24 @@ dkdv_kernel(BwdParams p) {
     const int qt0 = CAUSAL ? k0 / G::TILE : 0;
     TileRegs<D, S::NT> qr, dr;
     float lpre = 0.f, dpre = 0.f;
-    // statistics of row r of tile qt: rows past N get LSE +inf, so P = 0 there
+    bool rpre = false;
+    // statistics of row r of tile qt: rows past N get LSE +inf, so P = 0
+    // there.  The loaded values are first used when stored, so that the
+    // loads stay in flight during the tile's products.
     auto load_stats = [&](int qt) {
         if (tid < G::TILE) {
             const int r = qt * G::TILE + tid;
-            lpre = r < N ? lse[r] * kLog2e : __builtin_inff();
-            dpre = r < N ? delta[r] : 0.f;
+            rpre = r < N;
+            if (rpre) {
+                lpre = lse[r];
+                dpre = delta[r];
+            }
         }
     };
     auto store_stats = [&](int b) {
         if (tid < G::TILE) {
-            lses[b][tid] = lpre;
-            dls[b][tid] = dpre;
+            lses[b][tid] = rpre ? lpre * kLog2e : __builtin_inff();
+            dls[b][tid] = rpre ? dpre : 0.f;
         }
     };
     if (qt0 < nqt) {
