@@ -311,19 +311,21 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dq_kern
 // registers) and the K operand leave no room for V in registers at two waves
 // per SIMD, so eight waves (256 keys) share their V rows through LDS (68 KiB
 // beside the 68 KiB of Q / dO double buffers); at d = 64 four waves keep
-// both K and V in registers.
+// both K and V in registers, and with the Q / dO tiles copied straight into
+// LDS (168 VGPRs) three workgroups share a CU.
 template <int D>
 struct DkdvShape {
     static constexpr int WAVES = D == 128 ? 8 : 4;
     static constexpr int NT = 64 * WAVES;
     static constexpr int KEYS = 32 * WAVES;        // keys per workgroup
     static constexpr bool V_LDS = D == 128;
-    static constexpr int PER_CU = D == 128 ? 1 : 2;    // resident workgroups per CU
+    static constexpr bool DIRECT = D == 64;            // Q / dO tiles copied straight into LDS
+    static constexpr int PER_CU = D == 128 ? 1 : 3;    // resident workgroups per CU
 };
 
 template <class T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(DkdvShape<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(DkdvShape<D>::NT)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3, D == 128 ? 2 : 3))) dkdv_kernel(BwdParams p) {
     using G = Geo<D>;
     using S = DkdvShape<D>;
     // Q and dO tiles with their rows' LSE (base 2) and D, double-buffered
@@ -386,7 +388,6 @@ dkdv_kernel(BwdParams p) {
 
     const int nqt = (N + G::TILE - 1) / G::TILE;
     const int qt0 = CAUSAL ? k0 / G::TILE : 0;
-    TileRegs<D, S::NT> qr, dr;
     float lpre = 0.f, dpre = 0.f;
     bool rpre = false;
     // statistics of row r of tile qt: rows past N get LSE +inf, so P = 0
@@ -408,12 +409,41 @@ dkdv_kernel(BwdParams p) {
             dls[b][tid] = rpre ? dpre : 0.f;
         }
     };
+    // The next Q / dO tile goes HBM -> LDS during the current one.  At d = 64
+    // (S::DIRECT) the buffer unit copies it into LDS itself, in wave-sized
+    // 1 KiB pieces of the padded layout (16-byte chunk c at row c / CPR,
+    // chunk c % CPR of the row; the row's last chunk is padding and takes a
+    // copy of its first): that frees the 16 staging registers and lets three
+    // waves run per SIMD.  At d = 128 it passes through registers (TileRegs),
+    // which measured faster there.
+    constexpr int CPR = G::PITCH / 16, NPIECE = CPR * G::TILE / 64;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    TileRegs<D, S::NT> qr, dr;
+    auto fetch_tile = [&](uint8_t* qbuf, uint8_t* dbuf, int qt) {
+        if constexpr (S::DIRECT) {
+            for (int b = wv; b < NPIECE; b += S::WAVES) {
+                const int c = b * 64 + lane, row = c / CPR, ch = c % CPR;
+                const uint32_t off = (uint32_t)(((qt * G::TILE + row) * D + (ch < CPR - 1 ? ch : 0) * 8) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rq, (__attribute__((address_space(3))) void*)(qbuf + b * 1024), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rdo, (__attribute__((address_space(3))) void*)(dbuf + b * 1024), 16, off, 0, 0, 0);
+            }
+        } else {
+            qr.load(rq, qt * G::TILE, tid);
+            dr.load(rdo, qt * G::TILE, tid);
+        }
+    };
+    auto land_tile = [&](uint8_t* qbuf, uint8_t* dbuf) {   // register-staged copies into LDS
+        if constexpr (!S::DIRECT) {
+            qr.store(qbuf, tid);
+            dr.store(dbuf, tid);
+        }
+    };
     if (qt0 < nqt) {
-        qr.load(rq, qt0 * G::TILE, tid);
-        dr.load(rdo, qt0 * G::TILE, tid);
+        fetch_tile(qs[0], dos[0], qt0);
         load_stats(qt0);
-        qr.store(qs[0], tid);
-        dr.store(dos[0], tid);
+        land_tile(qs[0], dos[0]);
         store_stats(0);
     }
     __syncthreads();
@@ -421,8 +451,7 @@ dkdv_kernel(BwdParams p) {
         const int cur = (qt - qt0) & 1;
         const bool more = qt + 1 < nqt;
         if (more) {                            // next tile in flight during this one
-            qr.load(rq, (qt + 1) * G::TILE, tid);
-            dr.load(rdo, (qt + 1) * G::TILE, tid);
+            fetch_tile(qs[cur ^ 1], dos[cur ^ 1], qt + 1);
             load_stats(qt + 1);
         }
         const uint8_t* qc = qs[cur];
@@ -467,8 +496,7 @@ dkdv_kernel(BwdParams p) {
         }
         // the other buffers were last read before the previous barrier
         if (more) {
-            qr.store(qs[cur ^ 1], tid);
-            dr.store(dos[cur ^ 1], tid);
+            land_tile(qs[cur ^ 1], dos[cur ^ 1]);
             store_stats(cur ^ 1);
         }
         __syncthreads();
