@@ -179,6 +179,19 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, int splits, void* stream, int dtype);
 
 /*
+ * The number of key ranges for fa_fwd_split on the current device: with U =
+ * B * H * ceil(N / tile_q) the plain launch's (head, query tile) units and C
+ * the device's compute units, floor(C / U) without the mask (ranges that
+ * bring the units up to one per CU) and floor(2 C / U) under it (a causal
+ * launch with fewer than 2 C units waits on its longest rows), clamped to
+ * [1, min(16, key tiles)].  1 means that the plain fa_fwd is the faster
+ * call.  Writes *splits; FA_ERR_INVALID for a null pointer, a size <= 0 or
+ * causal not 0 or 1, FA_ERR_UNSUPPORTED for another dtype or d, FA_ERR_HIP
+ * if the device query fails (no HIP launch is made).
+ */
+int fa_fwd_split_count(int B, int H, int N, int d, int causal, int dtype, int* splits);
+
+/*
  * The (tile_q, tile_k) shape of the per-tile kernel for these parameters:
  * the tile of fp32-output launches and of launches too small for the
  * persistent kernels (fa_fwd_launch_tile gives the tile of any launch).

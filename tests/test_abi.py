@@ -265,6 +265,16 @@ def test_backward_noalloc_argument_checks():
         assert bwd(B=1, H=1, N=rows, **big) == fa.FA_ERR_HIP
 
 
+def test_split_count_argument_checks():
+    for args in [(0, 1, 100, 64, 0), (1, -1, 100, 64, 0), (1, 1, 0, 64, 0), (1, 1, 100, 64, 2)]:
+        assert fa.fa_fwd_split_count(*args, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_INVALID, args
+    assert fa.fa_fwd_split_count(1, 1, 100, 96, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_split_count(1, 1, 100, 64, 0, 9)[0] == fa.FA_ERR_UNSUPPORTED
+    assert fa.lib().fa_fwd_split_count(1, 1, 100, 64, 0, fa.FA_DTYPE_BF16, None) == fa.FA_ERR_INVALID
+    if NO_GPU:   # valid arguments: the device query fails here
+        assert fa.fa_fwd_split_count(1, 1, 100, 64, 0, fa.FA_DTYPE_BF16)[0] == fa.FA_ERR_HIP
+
+
 def test_split_argument_checks():
     OP, LP = 0x60000000, 0x70000000
 

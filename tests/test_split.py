@@ -98,6 +98,35 @@ def test_long_few_heads_and_peaked():
             assert_gates(errs, "bf16", f"long {values} head {h}")
 
 
+def test_split_count_rule():
+    """fa_fwd_split_count: ranges that bring the plain launch's (head, query
+    tile) units up to one per CU without the mask, to two per CU under it;
+    1 where the plain launch already fills the device."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bf = fa.FA_DTYPE_BF16
+    for (B, H, N, d, causal) in [(1, 1, 8192, 128, 0), (1, 1, 16384, 128, 0), (1, 2, 16384, 128, 0),
+                                 (2, 8, 4096, 128, 0), (1, 1, 32768, 128, 1), (1, 1, 16384, 128, 1),
+                                 (1, 2, 32768, 128, 1), (1, 32, 32768, 128, 1), (1, 1, 100, 64, 0), (16, 32, 1000, 64, 1)]:
+        st, tq, _ = fa.fa_fwd_tile_shape(bf, d, causal)
+        units = B * H * -(-N // tq)
+        want = max(1, min((2 * cus if causal else cus) // units, -(-N // 64), 16))
+        assert fa.fa_fwd_split_count(B, H, N, d, causal, bf) == (fa.FA_OK, want), (B, H, N, d, causal)
+    if cus == 256:    # the counts the measurements behind the rule chose on MI355X
+        assert fa.fa_fwd_split_count(1, 1, 8192, 128, 0, bf)[1] == 8
+        assert fa.fa_fwd_split_count(1, 2, 16384, 128, 0, bf)[1] == 2
+        assert fa.fa_fwd_split_count(1, 1, 32768, 128, 1, bf)[1] == 2
+        assert fa.fa_fwd_split_count(1, 32, 32768, 128, 1, bf)[1] == 1
+    # and attention_split without a count uses it
+    words = W.make_words((1, 1, 8192, 128), "bf16", "normal", 5)
+    qd, kd, vd = (to_dev(w, "bf16") for w in words)
+    o, lse, op, lp = fa.attention_split(qd, kd, vd, causal=False)
+    o1, lse1 = fa.attention(qd, kd, vd, causal=False)
+    torch.cuda.synchronize()
+    assert op.shape[0] == fa.fa_fwd_split_count(1, 1, 8192, 128, 0, bf)[1]
+    assert float((o.float() - o1.float()).abs().max()) <= 2 ** -6
+    assert float((lse - lse1).abs().max()) <= 1e-5
+
+
 def test_graph_replay():
     """The split-KV call (partial and merge kernels) captured into a HIP graph
     replays to the bits of the eager call."""

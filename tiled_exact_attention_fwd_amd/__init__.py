@@ -56,6 +56,7 @@ SIGNATURES = {
     "fa_build_info": (ctypes.c_char_p, []),
     "fa_standard_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I]),
     "fa_fwd_split": (_I, [_P] * 7 + [_I, _I, _I, _I, _F, _I, _I, _P, _I]),
+    "fa_fwd_split_count": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
     "fa_bwd_bf16": (_I, _BWD17),
     "fa_bwd_f16": (_I, _BWD17),
     "fa_bwd_f32": (_I, _BWD17),
@@ -156,17 +157,30 @@ def fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, causal, s
     return lib().fa_fwd_split(q, k, v, o, lse, o_part, lse_part, B, H, N, d, scale, causal, splits, stream, dtype)
 
 
-def attention_split(q, k, v, splits, causal=False, scale=None, stream=None):
+def fa_fwd_split_count(B, H, N, d, causal, dtype):
+    """Returns ``(status, splits)``: the key-range count the library suggests
+    for ``fa_fwd_split`` on the current device (1: the plain call is faster)."""
+    n = _I(0)
+    st = lib().fa_fwd_split_count(B, H, N, d, causal, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def attention_split(q, k, v, splits=None, causal=False, scale=None, stream=None):
     """Split-KV forward (include/fa_fwd.h ``fa_fwd_split``):
     returns ``(o, lse, o_part, lse_part)``, the merged outputs and the fp32
     per-range partials ([splits, B, H, N, d] and [splits, B, H, N]; only the
-    ranges the library used are written)."""
+    ranges the library used are written).  ``splits=None`` takes the count
+    ``fa_fwd_split_count`` suggests."""
     import math
     import torch
     for t in (q, k, v):
         if not t.is_contiguous() or not t.is_cuda or t.dtype != q.dtype or t.shape != q.shape or t.dim() != 4:
             raise ValueError("q, k, v must be contiguous device tensors of one [B, H, N, d] shape and dtype")
     B, H, N, d = q.shape
+    if splits is None:
+        st, splits = fa_fwd_split_count(B, H, N, d, int(bool(causal)), dtype_code(q.dtype))
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_split_count")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)

@@ -343,6 +343,26 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
 
 int fa_fwd_launch_tile(const fa_fwd_args* args, int* tile_q, int* tile_k) { return launch_tile(args, tile_q, tile_k); }
 
+int fa_fwd_split_count(int B, int H, int N, int d, int causal, int dtype, int* splits) {
+    if (!splits || B <= 0 || H <= 0 || N <= 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    int cus = 0;
+    const int st = check_device(&cus);
+    if (st != FA_OK) return st;
+    // the plain launch's work units: (head, query tile); without the mask
+    // they cost the same, so ranges that bring them up to one per CU fill
+    // the device; under the mask the longest unit costs twice the mean, so
+    // units below twice the CU count leave the launch waiting on its longest
+    // rows, and ranges cut them
+    const int tq = dtype == FA_DTYPE_F32 ? 64 : fa::tile_q16(causal != 0, d);
+    const uint64_t units = (uint64_t)B * H * ((uint64_t)(N + tq - 1) / tq);
+    const uint64_t want = (causal ? 2ull * cus : (uint64_t)cus) / units;
+    const uint64_t nk = ((uint64_t)N + 63) / 64;
+    *splits = (int)std::max<uint64_t>(1, std::min<uint64_t>(std::min<uint64_t>(want, nk), 16));
+    return FA_OK;
+}
+
 int fa_fwd_tile_shape(int dtype, int d, int causal, int* tile_q, int* tile_k) {
     if (!tile_q || !tile_k || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
