@@ -28,7 +28,10 @@
 // Each kernel recomputes S and dP for the pairs it visits, so the backward
 // runs seven N x N x d products per head where one that stored partial dQ
 // sums would run five; in exchange neither kernel needs atomics or a
-// reduction buffer and the results are deterministic.
+// reduction buffer and the results are deterministic.  (A five-product
+// kernel that adds each key block's share of dQ with float atomics measured
+// 4% faster at 4096 rows, d = 128, and half again slower at d = 64, where a
+// key block's dQ atomics meet half the matrix work.)
 //
 // MFMA layout (v_mfma_f32_32x32x16_{bf16,f16}, C = A B): lane (li, lh) of
 // the wave (li = lane % 32, lh = lane / 32) supplies A[li][8 lh .. 8 lh + 7]
