@@ -137,15 +137,17 @@ class ClockProbe:
 
 
 def window_summary(per, probe_mhz):
-    """Per-launch durations of one bracketed window, and the rate of the
-    shader cycle counter that probes read right before its first and right
-    after its last launch (mean over 64 CUs).  The probes run after the load
+    """Per-launch durations of the window that follows the bracketed one
+    (same launches, an event between consecutive ones), and the rate of the
+    shader cycle counter that probes read right before the bracketed
+    window's first and right after its last launch (mean over 64 CUs).  The probes run after the load
     has stopped: they read the clock the power manager has set, while inside
     the matrix-core-bound kernel the same counter advances more slowly (the
     chip's fast current limiter), so no fraction of a peak is derived from
     them."""
     out = {"launch_ms": {"first": round(per[0], 5), "max": round(max(per), 5), "min": round(min(per), 5),
-                         "mean": round(sum(per) / len(per), 5), "last": round(per[-1], 5)}}
+                         "mean": round(sum(per) / len(per), 5), "last": round(per[-1], 5),
+                         "how": "the same launches right after the bracketed window, an event between each two"}}
     if probe_mhz and all(probe_mhz):
         out["cycle_counter_mhz"] = {"before": round(probe_mhz[0][0], 1), "after": round(probe_mhz[1][0], 1),
                                     "cu_range_after": [round(probe_mhz[1][1], 1), round(probe_mhz[1][2], 1)]}
@@ -162,11 +164,14 @@ def prepare_forward(wl):
 
 
 def time_workload(wl, causal, steps, warmup, probe=None, tensors=None):
-    """Returns dict with ms_per_step (bracketed), the per-launch durations
-    inside the bracket (events between consecutive launches, so that they
-    tile the bracketed time exactly), the average shader clock over the
-    bracket (clock probes just outside it), and the per-launch mean/median/min
-    of a later run of individually timed launches."""
+    """Returns dict with ms_per_step (the bracketed window: `steps` launches
+    back to back between two events and nothing else on the stream), the
+    per-launch durations of a second window of as many launches right after
+    it (an event between consecutive launches, so that they tile that
+    window's time exactly; the events add about 0.6% to a step), the shader
+    clock just before and after the bracketed window (clock probes), and the
+    per-launch mean/median/min of a later run of individually timed
+    launches."""
     import torch
     import fa_workloads as W
     import tiled_exact_attention_fwd_amd as fa
@@ -187,21 +192,27 @@ def time_workload(wl, causal, steps, warmup, probe=None, tensors=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # bracketed region: exactly `steps` launches; ev[0] is its start, ev[steps]
-    # its end, and the events between consecutive launches split it per launch
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # bracketed region: exactly `steps` launches between two events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if probe:
         probe.mark(0, handle)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    if probe:
+        probe.mark(1, handle)
+    torch.cuda.synchronize()
+    bracket_ms = e0.elapsed_time(e1)
+    mhz = probe.mhz() if probe else None
+    # the same launches again, ev[0] .. ev[steps] splitting the window per launch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
         step()
         ev[i + 1].record(stream)
-    if probe:
-        probe.mark(1, handle)
     torch.cuda.synchronize()
-    bracket_ms = ev[0].elapsed_time(ev[steps])
     inside = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    mhz = probe.mhz() if probe else None
     # per-launch durations of a later run, each launch alone between two events
     ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for i in range(steps):
@@ -868,9 +879,9 @@ def main():
     r = time_workload(wl, False, a.steps, a.warmup, probe, fw_head)
     flops = wl.flops(False)
     value = flops / (r["ms_per_step"] * 1e-3) / 1e12
-    # the headline kernel's average launch duration over the timed region
-    mean_inside = sum(r["inside"]) / len(r["inside"])
-    achieved = flops / (mean_inside * 1e-3) / 1e12
+    # the headline kernel's average launch duration over the timed region:
+    # its only work is that kernel's launches
+    achieved = value
     cold = cold_cache(wl)
     traffic = traffic_for_kernel()
     out = {
@@ -907,7 +918,7 @@ def main():
                               "min": round(r["launch_min_ms"], 5),
                               "how": "a later run of the same launches, each alone between two events"},
         "hbm_min_gbs": round((4 * wl.B * wl.H * wl.N * wl.d * 2 + 4 * wl.B * wl.H * wl.N)
-                             / (mean_inside * 1e-3) / 1e9, 1),
+                             / (r["ms_per_step"] * 1e-3) / 1e9, 1),
         "kernel_hash": kernel_hash(),
     }
     if not a.no_cpu_baseline:
