@@ -86,6 +86,29 @@ def test_small(dtype, d, causal, N):
         assert max(errs.values()) <= 1e-4, errs
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        if rng.random() < 0.5:
+            N = int(rng.integers(1, 20)) * int(rng.choice([64, 128, 256])) + int(rng.choice([-1, 0, 1]))
+        else:
+            N = int(rng.integers(1, 2500))
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 5)), max(N, 1), int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f16"])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", _random_shapes(2025, 10))
+def test_random_shapes(B, H, N, d, dtype, causal):
+    """Seeded random shapes (N near the 64-, 128- and 256-row block
+    boundaries or anywhere up to 2500) against the gradient oracle."""
+    print(f"backward random shape {B}x{H}x{N}x{d} {dtype} causal={causal}", flush=True)
+    words, dwords = inputs((B, H, N, d), dtype, "normal", N)
+    errs, _ = check(words, dwords, dtype, causal, W.scale_for(d), what="random")
+    print(errs)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_spiky_causal(dtype):
     print(f"backward spiky {dtype}", flush=True)

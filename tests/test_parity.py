@@ -117,6 +117,31 @@ def test_small_f32(d, causal, N):
     print(f"f32 d={d} causal={causal} N={N}: {worst}")
 
 
+def _random_shapes(seed, count):
+    """Seeded shapes: N near tile boundaries (multiples of 64 and 128 plus or
+    minus one) or anywhere up to 3000, both head dimensions, both masks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        if rng.random() < 0.5:
+            N = int(rng.integers(1, 24)) * int(rng.choice([64, 128])) + int(rng.choice([-1, 0, 1]))
+        else:
+            N = int(rng.integers(1, 3001))
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 6)), max(N, 1), int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f16"])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", _random_shapes(2024, 16))
+def test_random_shapes(B, H, N, d, dtype, causal):
+    """Seeded random shapes against the oracle on every head and row, with
+    the tile counts of the launched kernel."""
+    print(f"random shape {B}x{H}x{N}x{d} {dtype} causal={causal}", flush=True)
+    words = W.make_words((B, H, N, d), dtype, "normal", N)
+    worst, _ = check_against_oracle(words, dtype, causal, W.scale_for(d), what="random")
+    print(worst)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_spiky_and_scales(dtype):
     """Running-max rescales (a few keys x8), a negative scale, a large scale
