@@ -142,6 +142,35 @@ def test_random_shapes(B, H, N, d, dtype, causal):
     print(worst)
 
 
+def _random_persistent_shapes(seed, count):
+    """Seeded d = 128 shapes with enough query tiles for the persistent
+    kernels (more 256-row tiles, or causal pairs of them, than CUs)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        causal = i % 2 == 1
+        if causal:   # an even number of 256-row tiles: the paired causal kernel
+            wt = 2 * int(rng.integers(1, 6))
+            N = 256 * wt - int(rng.integers(0, 256))
+            heads = 512 // wt + int(rng.integers(1, 120))
+        else:
+            N = int(rng.integers(300, 2600))
+            heads = int(rng.integers(96, 400))
+        out.append((1, heads, N, str(rng.choice(["bf16", "f16"])), causal))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,dtype,causal", _random_persistent_shapes(2026, 6))
+def test_random_persistent_shapes(B, H, N, dtype, causal):
+    """Seeded shapes on the persistent kernels' path: three whole heads
+    (first, middle, last) against the oracle, counts of the launched kernel."""
+    print(f"random persistent shape {B}x{H}x{N}x128 {dtype} causal={causal}", flush=True)
+    words = W.make_words((B, H, N, 128), dtype, "normal", N + H)
+    heads = [(0, 0), (0, H // 2), (0, H - 1)]
+    worst, _ = check_against_oracle(words, dtype, causal, W.scale_for(128), heads=heads, what="random persistent")
+    print(worst)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_spiky_and_scales(dtype):
     """Running-max rescales (a few keys x8), a negative scale, a large scale
