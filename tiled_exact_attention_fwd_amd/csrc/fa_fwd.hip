@@ -169,7 +169,8 @@ int run(const fa_fwd_args* a) {
     p.heads = a->B * a->H;
     p.total = p.heads * p.tiles_q;
     const int resident = a->dtype == FA_DTYPE_F32 ? fa::resident32() : fa::resident16(a->causal != 0, a->d);
-    p.group = fa::causal_group(p.heads, p.tiles_q, cus / fa::kNumXcd * resident);
+    p.group = a->dtype == FA_DTYPE_F32 ? fa::causal_group(p.heads, p.tiles_q, cus / fa::kNumXcd * resident)
+                                        : fa::fwd_causal_group(p.heads);
     // softmax in base 2: exp(scale * s) = 2^(s * |scale| * log2 e) after a sign
     // flip of Q for negative scales; FLT_MIN keeps -inf * c at -inf for scale 0
     p.c = std::fmax(std::fabs(a->scale) * 1.4426950408889634f, FLT_MIN);

@@ -197,18 +197,28 @@ __device__ __forceinline__ TileId tile_of(int bid, const FwdParams& p) {
     return {bid - rank * p.heads, p.tiles_q - 1 - rank};
 }
 
-// Heads per group of the causal order above: enough for the group's query
-// tiles to fill the workgroup slots of one XCD twice, at most the XCD's
-// heads.  (Measured on the 4096-row, 64-head causal launch: groups of 2
-// heads, which fill the slots once, leave the last group's long tiles
-// running alone at the end; 4 heads balance as well as all 8.  On the
-// 1000-row, 512-head launch groups of 16 heads beat 8 and 64: larger groups
-// spread each head's K and V reuse out of the L2.)
+// Heads per group of a causal order like the one above: enough for the
+// group's blocks to fill the workgroup slots of one XCD twice, at most the
+// XCD's heads (the backward's block orders; measured there against groups of
+// 1, 2 and all of an XCD's heads).
 inline int causal_group(int heads, int tiles_q, int slots_per_xcd) {
     if (heads % kNumXcd != 0) return 1;
     const int g = (2 * slots_per_xcd + tiles_q - 1) / tiles_q;
     const int hpx = heads / kNumXcd;
     return g < 1 ? 1 : (g > hpx ? hpx : g);
+}
+
+// Heads per group of the 16-bit per-tile forward's causal order: 16, or all
+// of an XCD's heads when it has fewer.  Smaller groups leave the last
+// group's long tiles running alone at the end (4096 rows, 64 heads: groups of
+// 2 heads); larger ones spread each head's K and V reuse out of the L2.  In
+// interleaved A/B runs 16 was the best or within noise of it at every shape
+// measured (d = 64: 1000 rows x 512 heads, 2048 x 512, 4096 x 64,
+// 512 x 1024, 2000 x 128; d = 128: 3800 x 64, 1000 x 256), up to 6% ahead
+// of groups sized to fill the slots twice.
+inline int fwd_causal_group(int heads) {
+    if (heads % kNumXcd != 0) return 1;
+    return min(16, heads / kNumXcd);
 }
 
 // ---------------------------------------------------------------------------
