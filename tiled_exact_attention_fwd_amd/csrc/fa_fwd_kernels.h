@@ -214,8 +214,8 @@ inline int causal_group(int heads, int tiles_q, int slots_per_xcd) {
 // 2 heads); larger ones spread each head's K and V reuse out of the L2.  In
 // interleaved A/B runs 16 was the best or within noise of it at every shape
 // measured (d = 64: 1000 rows x 512 heads, 2048 x 512, 4096 x 64,
-// 512 x 1024, 2000 x 128; d = 128: 3800 x 64, 1000 x 256), up to 6% ahead
-// of groups sized to fill the slots twice.
+// 512 x 1024, 2000 x 128; d = 128: 3800 x 64, 1000 x 256), 0-6% ahead of
+// groups sized to fill the slots twice.
 inline int fwd_causal_group(int heads) {
     if (heads % kNumXcd != 0) return 1;
     return min(16, heads / kNumXcd);
